@@ -1,0 +1,155 @@
+// Host-side entry points of libqw that launch nothing: version, status text,
+// buffer sizes, format constants, and the device check used by the others.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "qw_internal.h"
+
+#pragma STDC FP_CONTRACT OFF
+
+namespace qw {
+
+namespace {
+struct DevInfo {
+  int state = 0;  // 0 unknown, 1 ok, 2 not gfx950
+  int cus = 0;
+};
+DevInfo g_dev[64];
+std::mutex g_dev_mu;
+
+float g_nf4[16];
+std::once_flag g_nf4_once;
+
+// Standard normal CDF from the complementary error function.
+double norm_cdf(double x) { return 0.5 * erfc(-x / sqrt(2.0)); }
+
+// Inverse standard normal CDF: bisection to bracket, then Newton steps on
+// Phi(x) - p with derivative phi(x).
+double norm_ppf(double p) {
+  double lo = -40.0, hi = 40.0;
+  for (int i = 0; i < 200 && hi - lo > 1e-12; ++i) {
+    double mid = 0.5 * (lo + hi);
+    if (norm_cdf(mid) < p) lo = mid; else hi = mid;
+  }
+  double x = 0.5 * (lo + hi);
+  const double inv_sqrt_2pi = 0.39894228040143267794;
+  for (int i = 0; i < 4; ++i) {
+    double pdf = inv_sqrt_2pi * exp(-0.5 * x * x);
+    x = x - (norm_cdf(x) - p) / pdf;
+  }
+  return x;
+}
+
+void build_nf4() {
+  // "Fontes" of the AirQuant README cites QLoRA for NF4; the levels are the
+  // normalised normal quantiles described in qw.h.
+  const double delta = 1.0 - 0.5 * (1.0 / 32.0 + 1.0 / 30.0);
+  double v[16];
+  int n = 0;
+  {
+    double step = (0.5 - delta) / 8.0;
+    for (int i = 0; i < 8; ++i) v[n++] = norm_ppf((double)i * step + delta);
+  }
+  {
+    double step = (0.5 - delta) / 7.0;
+    for (int i = 0; i < 7; ++i) v[n++] = -norm_ppf((double)i * step + delta);
+  }
+  v[n++] = 0.0;
+  // insertion sort, ascending
+  for (int i = 1; i < 16; ++i) {
+    double t = v[i];
+    int j = i - 1;
+    while (j >= 0 && v[j] > t) { v[j + 1] = v[j]; --j; }
+    v[j + 1] = t;
+  }
+  double mx = v[15];
+  for (int i = 0; i < 16; ++i) g_nf4[i] = (float)(v[i] / mx);
+}
+}  // namespace
+
+const float *nf4_levels_host() {
+  std::call_once(g_nf4_once, build_nf4);
+  return g_nf4;
+}
+
+qw_status current_device(int *cu_count) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return QW_ERR_NO_DEVICE;
+  if (dev < 0 || dev >= 64) return QW_ERR_NO_DEVICE;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DevInfo &d = g_dev[dev];
+  if (d.state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return QW_ERR_NO_DEVICE;
+    d.state = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    d.cus = prop.multiProcessorCount;
+  }
+  if (d.state != 1) return QW_ERR_NO_DEVICE;
+  if (cu_count) *cu_count = d.cus;
+  return QW_OK;
+}
+
+}  // namespace qw
+
+extern "C" {
+
+int qw_abi_version(void) { return QW_ABI_VERSION; }
+
+const char *qw_status_str(qw_status s) {
+  switch (s) {
+    case QW_OK: return "ok";
+    case QW_ERR_INVALID_ARG: return "invalid argument";
+    case QW_ERR_ALIGNMENT: return "device pointer not 16-byte aligned";
+    case QW_ERR_UNSUPPORTED: return "unsupported request";
+    case QW_ERR_HIP: return "HIP runtime error";
+    case QW_ERR_NO_DEVICE: return "no gfx950 device is current";
+  }
+  return "unknown status";
+}
+
+qw_status qw_packed_sizes(qw_format fmt, int N, int K, int n_out,
+                          size_t *codes_bytes, size_t *scales_bytes,
+                          size_t *out_w_bytes, int *n_out_pad) {
+  if (N <= 0 || K <= 0 || n_out < 0 || n_out >= K) return QW_ERR_INVALID_ARG;
+  size_t c = 0, s = 0, o = 0;
+  int pad = 0;
+  if (fmt == QW_FMT_2BIT_G32) {
+    if (K % 32) return QW_ERR_INVALID_ARG;
+    c = (size_t)N * (size_t)(K / 4);
+    s = (size_t)N * (size_t)(K / 32) * 4;
+    pad = n_out ? qw::pad8(n_out) : 0;
+    o = (size_t)N * (size_t)pad * 2;
+  } else if (fmt == QW_FMT_NF4_B64) {
+    if (K % 64 || n_out != 0) return QW_ERR_INVALID_ARG;
+    c = (size_t)N * (size_t)(K / 2);
+    s = (size_t)N * (size_t)(K / 64) * 4;
+  } else {
+    return QW_ERR_INVALID_ARG;
+  }
+  if (codes_bytes) *codes_bytes = c;
+  if (scales_bytes) *scales_bytes = s;
+  if (out_w_bytes) *out_w_bytes = o;
+  if (n_out_pad) *n_out_pad = pad;
+  return QW_OK;
+}
+
+int qw_outlier_count(int K, double frac) {
+  if (K < 0 || !(frac >= 0.0 && frac < 1.0)) return -1;
+  return (int)floor(frac * (double)K);
+}
+
+qw_status qw_codebook_2bit(float *out) {
+  if (!out) return QW_ERR_INVALID_ARG;
+  out[0] = -1.52f; out[1] = -0.45f; out[2] = 0.45f; out[3] = 1.52f;
+  return QW_OK;
+}
+
+qw_status qw_nf4_levels(float *out) {
+  if (!out) return QW_ERR_INVALID_ARG;
+  memcpy(out, qw::nf4_levels_host(), 16 * sizeof(float));
+  return QW_OK;
+}
+
+}  // extern "C"

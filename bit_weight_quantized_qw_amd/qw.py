@@ -1,0 +1,276 @@
+"""Thin ctypes binding over libqw.so (C ABI in include/qw.h).
+
+Argument marshalling only: every step of quantization, packing and the
+products runs in the library's HIP kernels. Torch tensors supply device
+memory and the current stream. The functions carry the C names; the
+``PackedWeight`` holder owns the torch buffers one packed matrix needs.
+
+If libqw.so is missing this module raises on first use; there is no
+fallback path.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqw.so")
+
+QW_OK, QW_ERR_INVALID_ARG, QW_ERR_ALIGNMENT, QW_ERR_UNSUPPORTED, QW_ERR_HIP, QW_ERR_NO_DEVICE = range(6)
+QW_FMT_2BIT_G32, QW_FMT_NF4_B64 = 1, 2
+QW_DT_F16, QW_DT_BF16, QW_DT_F32 = 1, 2, 3
+QW_SCORE_MEANABS, QW_SCORE_L2 = 1, 2
+
+# every function declared in include/qw.h
+EXPORTS = [
+    "qw_abi_version", "qw_status_str", "qw_packed_sizes", "qw_outlier_count",
+    "qw_codebook_2bit", "qw_nf4_levels", "qw_select_outliers", "qw_pack",
+    "qgemv_2bit", "qgemv_nf4", "qgemv_2bit_grouped", "qgemm_prefill",
+]
+
+
+class QwError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {qw_status_str(status)} (status {status})")
+
+
+class qw_weight(ctypes.Structure):
+    _fields_ = [
+        ("format", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+        ("n_out", ctypes.c_int32), ("n_out_pad", ctypes.c_int32),
+        ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+        ("out_idx", ctypes.c_void_p), ("out_w", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load libqw.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing; build it with "
+                           "`python -m bit_weight_quantized_qw_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    c_i, c_d, c_p, c_sz = ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_size_t
+    W = ctypes.POINTER(qw_weight)
+    sig = {
+        "qw_abi_version": (c_i, []),
+        "qw_status_str": (ctypes.c_char_p, [c_i]),
+        "qw_packed_sizes": (c_i, [c_i, c_i, c_i, c_i, ctypes.POINTER(c_sz), ctypes.POINTER(c_sz),
+                                  ctypes.POINTER(c_sz), ctypes.POINTER(c_i)]),
+        "qw_outlier_count": (c_i, [c_i, c_d]),
+        "qw_codebook_2bit": (c_i, [ctypes.POINTER(ctypes.c_float)]),
+        "qw_nf4_levels": (c_i, [ctypes.POINTER(ctypes.c_float)]),
+        "qw_select_outliers": (c_i, [c_p, c_i, c_i, c_p, c_i, c_d, c_i, c_p, c_p]),
+        "qw_pack": (c_i, [c_p, W, c_p]),
+        "qgemv_2bit": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
+        "qgemv_nf4": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
+        "qgemv_2bit_grouped": (c_i, [W, c_i, c_p, c_i, ctypes.POINTER(c_p), c_i, c_p]),
+        "qgemm_prefill": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(status, where):
+    if status != QW_OK:
+        raise QwError(status, where)
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+# ---------------------------------------------------------------- host calls
+
+def qw_abi_version():
+    return lib().qw_abi_version()
+
+
+def qw_status_str(status):
+    return lib().qw_status_str(int(status)).decode()
+
+
+def qw_packed_sizes(fmt, N, K, n_out=0):
+    cb, sb, ob = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    pad = ctypes.c_int()
+    _check(lib().qw_packed_sizes(fmt, N, K, n_out, ctypes.byref(cb), ctypes.byref(sb),
+                                 ctypes.byref(ob), ctypes.byref(pad)), "qw_packed_sizes")
+    return cb.value, sb.value, ob.value, pad.value
+
+
+def qw_outlier_count(K, frac):
+    return lib().qw_outlier_count(int(K), float(frac))
+
+
+def qw_codebook_2bit():
+    out = (ctypes.c_float * 4)()
+    _check(lib().qw_codebook_2bit(out), "qw_codebook_2bit")
+    return np.array(out[:], dtype=np.float32)
+
+
+def qw_nf4_levels():
+    out = (ctypes.c_float * 16)()
+    _check(lib().qw_nf4_levels(out), "qw_nf4_levels")
+    return np.array(out[:], dtype=np.float32)
+
+
+# -------------------------------------------------------------- packed weight
+
+class PackedWeight:
+    """Device buffers of one packed matrix (torch tensors, caller-owned)."""
+
+    def __init__(self, fmt, N, K, n_out=0, device="cuda"):
+        import torch
+        cb, sb, ob, pad = qw_packed_sizes(fmt, N, K, n_out)
+        self.format, self.N, self.K, self.n_out, self.n_out_pad = fmt, N, K, n_out, pad
+        self.codes = torch.empty(cb, dtype=torch.uint8, device=device)
+        self.scales = torch.empty(sb, dtype=torch.uint8, device=device)
+        self.out_idx = torch.empty(max(n_out, 1), dtype=torch.int32, device=device) if n_out else None
+        self.out_w = torch.empty(max(ob // 2, 1), dtype=torch.int16, device=device) if n_out else None
+
+    def view(self):
+        return qw_weight(self.format, self.N, self.K, self.n_out, self.n_out_pad,
+                         self.codes.data_ptr(), self.scales.data_ptr(),
+                         self.out_idx.data_ptr() if self.out_idx is not None else None,
+                         self.out_w.data_ptr() if self.out_w is not None else None)
+
+    def nbytes(self):
+        n = self.codes.numel() + self.scales.numel()
+        if self.n_out:
+            n += self.out_idx.numel() * 4 + self.out_w.numel() * 2
+        return n
+
+    # host copies in the oracle's array shapes
+    def host_codes(self):
+        return self.codes.cpu().numpy().reshape(self.N, -1)
+
+    def host_scales(self):
+        a = self.scales.cpu().numpy()
+        if self.format == QW_FMT_2BIT_G32:
+            return a.view(np.float16).reshape(self.N, self.K // 32, 2)
+        return a.view(np.float32).reshape(self.N, self.K // 64)
+
+    def host_out_w(self):
+        if not self.n_out:
+            return np.zeros((self.N, 0), np.float16)
+        return self.out_w.cpu().numpy().view(np.float16).reshape(self.N, self.n_out_pad)
+
+
+def _need(t, dtype, name, ndim=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+
+
+def qw_select_outliers(W, X_prof, frac, score=QW_SCORE_MEANABS):
+    import torch
+    _need(W, torch.float32, "W", 2)
+    _need(X_prof, torch.float32, "X_prof", 2)
+    N, K = W.shape
+    n = qw_outlier_count(K, frac)
+    if n < 0:
+        raise ValueError("frac must be in [0, 1)")
+    out = torch.empty(max(n, 1), dtype=torch.int32, device=W.device)
+    _check(lib().qw_select_outliers(_ptr(W), N, K, _ptr(X_prof), X_prof.shape[0], float(frac),
+                                    int(score), _ptr(out), _stream()), "qw_select_outliers")
+    return out[:n]
+
+
+def qw_pack(W, fmt=QW_FMT_2BIT_G32, out_idx=None):
+    """Quantize and pack fp32 W (N, K) on the device; returns PackedWeight."""
+    import torch
+    _need(W, torch.float32, "W", 2)
+    N, K = W.shape
+    n_out = 0 if out_idx is None else int(out_idx.numel())
+    pw = PackedWeight(fmt, N, K, n_out, device=W.device)
+    if n_out:
+        _need(out_idx, torch.int32, "out_idx", 1)
+        ok = bool(((out_idx[1:] > out_idx[:-1]).all() & (out_idx[0] >= 0) & (out_idx[-1] < K)).item())
+        if not ok:
+            raise ValueError("out_idx must be strictly ascending channels in [0, K)")
+        pw.out_idx.copy_(out_idx)
+    v = pw.view()
+    _check(lib().qw_pack(_ptr(W), ctypes.byref(v), _stream()), "qw_pack")
+    return pw
+
+
+_OUT = {"f16": QW_DT_F16, "bf16": QW_DT_BF16, "f32": QW_DT_F32}
+
+
+def _dt(torch_dtype):
+    import torch
+    m = {torch.float16: QW_DT_F16, torch.bfloat16: QW_DT_BF16, torch.float32: QW_DT_F32}
+    return m[torch_dtype]
+
+
+def qgemv_2bit(pw, x, out_dtype=None, out=None):
+    import torch
+    _need(x, torch.float16, "x", 2)
+    out_dtype = out_dtype or torch.float16
+    B = x.shape[0]
+    y = out if out is not None else torch.empty((B, pw.N), dtype=out_dtype, device=x.device)
+    v = pw.view()
+    _check(lib().qgemv_2bit(ctypes.byref(v), _ptr(x), B, _ptr(y), _dt(y.dtype), _stream()),
+           "qgemv_2bit")
+    return y
+
+
+def qgemv_nf4(pw, x, out_dtype=None, out=None):
+    import torch
+    _need(x, torch.float16, "x", 2)
+    out_dtype = out_dtype or torch.float16
+    B = x.shape[0]
+    y = out if out is not None else torch.empty((B, pw.N), dtype=out_dtype, device=x.device)
+    v = pw.view()
+    _check(lib().qgemv_nf4(ctypes.byref(v), _ptr(x), B, _ptr(y), _dt(y.dtype), _stream()),
+           "qgemv_nf4")
+    return y
+
+
+def qgemv_2bit_grouped(pws, x, out_dtype=None, outs=None):
+    import torch
+    _need(x, torch.float16, "x", 2)
+    out_dtype = out_dtype or torch.float16
+    B = x.shape[0]
+    n = len(pws)
+    ys = outs if outs is not None else [
+        torch.empty((B, p.N), dtype=out_dtype, device=x.device) for p in pws]
+    arr = (qw_weight * n)(*[p.view() for p in pws])
+    yp = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
+    _check(lib().qgemv_2bit_grouped(arr, n, _ptr(x), B, yp, _dt(ys[0].dtype), _stream()),
+           "qgemv_2bit_grouped")
+    return ys
+
+
+def qgemm_prefill(pw, X, out_dtype=None, out=None):
+    import torch
+    _need(X, torch.bfloat16, "X", 2)
+    out_dtype = out_dtype or torch.bfloat16
+    M = X.shape[0]
+    Y = out if out is not None else torch.empty((M, pw.N), dtype=out_dtype, device=X.device)
+    v = pw.view()
+    _check(lib().qgemm_prefill(ctypes.byref(v), _ptr(X), M, _ptr(Y), _dt(Y.dtype), _stream()),
+           "qgemm_prefill")
+    return Y

@@ -1,0 +1,197 @@
+/*
+ * qw.h -- C ABI of libqw: matrix products against block-wise low-bit
+ * quantized weights with the dequantization fused into the product, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Formats (defined by the pages this library implements):
+ *
+ *  QW_FMT_2BIT_G32 -- "On-The-Fly Weight Synthesizer (OTF-LLM Engine v4.0)":
+ *    adaptive non-uniform 2-bit code. Each weight is one of four Lloyd-Max
+ *    Gaussian centroids C = {-1.52, -0.45, +0.45, +1.52} (section 2; fp32
+ *    constants), mapped through a per-group scale and offset fitted by
+ *    closed-form least squares over groups of 32 along K (section 3):
+ *        w_hat[n][k] = S[n][k/32] * C[q[n][k]] + Z[n][k/32].
+ *    Four codes per byte ("Key v4.0 Innovations"). Optional FP16 outlier
+ *    anchors (section 4): input channels out_idx[0..n_out) whose weights are
+ *    kept exactly in fp16; the 2-bit code of those columns is stored but the
+ *    products use the anchors instead.
+ *  QW_FMT_NF4_B64 -- "AirQuant" README, "Fundamentacao Teorica e
+ *    Arquitetura" item 2: NormalFloat4 (QLoRA) with a per-block absmax:
+ *        w_hat[n][k] = absmax[n][k/64] * L[q[n][k]],
+ *    L = 16 normalised N(0,1) quantiles in [-1, 1] (see qw_nf4_levels).
+ *
+ * Memory layout in device memory (all row-major, rows = output features n):
+ *  2-bit codes   uint8 [N][K/4]; byte j holds elements 4j..4j+3, element
+ *                4j+t in bits 2t..2t+1; code value q indexes C ascending.
+ *  2-bit scales  uint16 pairs [N][K/32][2]: [.][.][0] = S, [.][.][1] = Z,
+ *                both IEEE fp16 bit patterns.
+ *  anchors       out_idx int32 [n_out], strictly ascending, in [0, K);
+ *                out_w fp16 [N][n_out_pad], n_out_pad = n_out rounded up to a
+ *                multiple of 8, padding zero.
+ *  NF4 codes     uint8 [N][K/2]; low nibble = element 2j, high = 2j+1.
+ *  NF4 scales    float [N][K/64] (absmax per block of 64 along K).
+ *
+ * Conventions for every entry point:
+ *  - pointers documented "device" must point to device memory of the
+ *    current HIP device; "host" pointers to host memory. The caller owns
+ *    and frees all memory; nothing is retained after the call returns.
+ *  - ``stream`` is a hipStream_t passed as void* (NULL = default stream).
+ *    Device work is only enqueued; no entry point synchronizes, except
+ *    qw_select_outliers (see there).
+ *  - arguments are validated on the host before anything is enqueued; on
+ *    any error nothing is enqueued and the status says why. A failed launch
+ *    returns QW_ERR_HIP. No entry point aborts or throws.
+ *  - results are deterministic: the same inputs give the same bits.
+ *  - device base pointers must be 16-byte aligned (QW_ERR_ALIGNMENT).
+ */
+#ifndef QW_H_
+#define QW_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QW_ABI_VERSION 1
+
+typedef enum {
+  QW_OK = 0,
+  QW_ERR_INVALID_ARG = 1, /* a size, count, enum or pointer is out of range */
+  QW_ERR_ALIGNMENT = 2,   /* a device pointer is not 16-byte aligned */
+  QW_ERR_UNSUPPORTED = 3, /* valid request this build does not implement */
+  QW_ERR_HIP = 4,         /* a HIP runtime call or launch failed */
+  QW_ERR_NO_DEVICE = 5    /* no gfx950 device is current */
+} qw_status;
+
+typedef enum { QW_FMT_2BIT_G32 = 1, QW_FMT_NF4_B64 = 2 } qw_format;
+typedef enum { QW_DT_F16 = 1, QW_DT_BF16 = 2, QW_DT_F32 = 3 } qw_dtype;
+
+/* Outlier channel score ("Profile-Guided Activation Outliers", section 4):
+ * MEANABS = mean_n |W[n][c]| * mean_p |X[p][c]| (the |W| x |X| shorthand of
+ * the page's title and feature list); L2 = ||W[:,c]||_2 * mean_p |X[p][c]|
+ * (the section-4 equation). */
+typedef enum { QW_SCORE_MEANABS = 1, QW_SCORE_L2 = 2 } qw_score;
+
+/* Non-owning view of one packed weight matrix. All pointers are device
+ * pointers owned by the caller. For NF4, out_idx/out_w are unused and n_out
+ * must be 0. */
+typedef struct {
+  int32_t format;     /* qw_format */
+  int32_t N, K;       /* output features, input features */
+  int32_t n_out;      /* number of fp16 anchor channels (2-bit only) */
+  int32_t n_out_pad;  /* row stride of out_w in elements (multiple of 8) */
+  uint8_t *codes;     /* see layout above */
+  void *scales;       /* 2-bit: uint16 [N][K/32][2]; NF4: float [N][K/64] */
+  int32_t *out_idx;   /* [n_out] or NULL when n_out == 0 */
+  uint16_t *out_w;    /* fp16 [N][n_out_pad] or NULL when n_out == 0 */
+} qw_weight;
+
+/* Version of this ABI (QW_ABI_VERSION). */
+int qw_abi_version(void);
+
+/* Static text for a status code. Never NULL. */
+const char *qw_status_str(qw_status s);
+
+/* Bytes the caller must allocate for a packed matrix of the given format
+ * and shape, and the anchor row stride. Host only; any output pointer may
+ * be NULL. Errors: QW_ERR_INVALID_ARG if N, K <= 0, K not a multiple of the
+ * group/block size (32 for 2-bit, 64 for NF4), n_out < 0, n_out >= K, or
+ * n_out > 0 for NF4. */
+qw_status qw_packed_sizes(qw_format fmt, int N, int K, int n_out,
+                          size_t *codes_bytes, size_t *scales_bytes,
+                          size_t *out_w_bytes, int *n_out_pad);
+
+/* Number of anchor channels for a fraction of K: floor(frac * K) in double
+ * precision (section 4 keeps the top 3.5%). Returns -1 if K < 0 or frac is
+ * outside [0, 1). Host only. */
+int qw_outlier_count(int K, double frac);
+
+/* The four 2-bit centroids (section 2 of the OTF-LLM page) as fp32, into
+ * host array out[4]. */
+qw_status qw_codebook_2bit(float *out);
+
+/* The 16 NF4 levels the library uses, ascending, as fp32, into host array
+ * out[16]. Built on the host at first use from normal quantiles: 8 positive
+ * at probabilities evenly spaced from delta down to 1/2 (exclusive), 7
+ * negative likewise, plus 0, divided by the largest;
+ * delta = 1 - (1/32 + 1/30)/2. */
+qw_status qw_nf4_levels(float *out);
+
+/* Profile-guided outlier selection (section 4 of the OTF-LLM page).
+ *   W      device fp32 [N][K]  weights
+ *   X_prof device fp32 [P][K]  calibration activations (P >= 1)
+ *   frac   fraction of channels to keep, n = floor(frac*K) (0 <= frac < 1)
+ *   out_idx device int32 [n]   receives the n highest-scoring channels in
+ *          ascending order; ties in score go to the lower channel.
+ * Scores are fp64 with sequential sums over rows. Uses a device scratch
+ * buffer of K*12 bytes that it allocates and frees with the stream-ordered
+ * allocator on ``stream``. Errors: INVALID_ARG for bad sizes or NULL
+ * pointers, HIP if the allocation or a launch fails. */
+qw_status qw_select_outliers(const float *W, int N, int K, const float *X_prof,
+                             int P, double frac, qw_score score,
+                             int32_t *out_idx, void *stream);
+
+/* Quantize and pack fp32 weights into ``dst`` (buffers allocated by the
+ * caller with the sizes from qw_packed_sizes; dst->format, N, K, n_out,
+ * n_out_pad must describe them).
+ *   W        device fp32 [N][K]
+ *   dst->out_idx (2-bit, n_out > 0) device int32 [n_out], strictly ascending;
+ *            those columns are zeroed before the fit and copied to out_w
+ *            rounded to fp16 (nearest-even).
+ * 2-bit: per group of 32 along K, in fp64 without fused multiply-add:
+ * mean m and population variance v; code q = (w-m >= 0 ? 2 : 1) moved to
+ * the outer level (3 or 0) when (w-m)^2 > t^2 v with t = (C[2]+C[3])/2;
+ * S = sum (w-m)(c-cbar) / (sum (c-cbar)^2 + 1e-8), Z = m - S cbar
+ * (section 3); S and Z rounded once to fp16 (nearest-even, subnormals kept).
+ * NF4: per block of 64, absmax a = max |w|; q = number of level midpoints
+ * t_j with w > t_j * a (nearest level, ties low); a == 0 gives q = 7.
+ * The result is bit-identical to the reference quantizer. Errors:
+ * INVALID_ARG, ALIGNMENT, HIP. out_idx ordering is not checked here (the
+ * Python binding checks it). */
+qw_status qw_pack(const float *W, const qw_weight *dst, void *stream);
+
+/* Decode GEMV for the 2-bit format:
+ *   y[b][n] = sum_k x_R[b][k] w_hat[n][k] + sum_o x[b][out_idx[o]] out_w[n][o]
+ * for b < B, where x_R is x with the anchor channels set to zero.
+ *   x  device fp16 [B][K], 1 <= B <= 8
+ *   y  device [B][N], fp16 (QW_DT_F16, rounded nearest-even) or fp32
+ * Accumulation is fp32. Codes are decoded in registers; nothing is
+ * materialized. y must not alias x. Errors: INVALID_ARG (format mismatch,
+ * B, dtype), ALIGNMENT, HIP. */
+qw_status qgemv_2bit(const qw_weight *w, const void *x, int B, void *y,
+                     qw_dtype y_dtype, void *stream);
+
+/* Decode GEMV for NF4: y[b][n] = sum_k x[b][k] w_hat[n][k]. Same argument
+ * conventions as qgemv_2bit. */
+qw_status qgemv_nf4(const qw_weight *w, const void *x, int B, void *y,
+                    qw_dtype y_dtype, void *stream);
+
+/* Several 2-bit decode GEMVs that share one input x (for example the q, k
+ * and v projections of one attention block), in one launch:
+ *   y_i = qgemv_2bit(w_i, x) for i < count (count <= 4).
+ * All w_i must have the same K; y_i have their own N_i. Same conventions as
+ * qgemv_2bit; ws and ys are host arrays of count entries. */
+qw_status qgemv_2bit_grouped(const qw_weight *ws, int count, const void *x,
+                             int B, void *const *ys, qw_dtype y_dtype,
+                             void *stream);
+
+/* Prefill GEMM: Y[m][n] = sum_k X[m][k] w_bf16[n][k] with
+ * w_bf16 = bf16(fp32(S*C[q]+Z)) (one fused multiply-add, then nearest-even)
+ * for 2-bit, bf16(fp32(absmax*L[q])) for NF4; 2-bit anchor columns use
+ * bf16(out_w). Tiles of the dequantized weight are staged through LDS into
+ * bf16 matrix-core instructions with fp32 accumulation.
+ *   X  device bf16 [M][K], M >= 1
+ *   Y  device [M][N], bf16 (QW_DT_BF16, nearest-even of the fp32 result) or
+ *      fp32 (QW_DT_F32)
+ * Requires K to be a multiple of 64. Errors: INVALID_ARG, ALIGNMENT,
+ * UNSUPPORTED, HIP. */
+qw_status qgemm_prefill(const qw_weight *w, const void *X, int M, void *Y,
+                        qw_dtype y_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QW_H_ */

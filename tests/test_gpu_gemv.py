@@ -1,0 +1,159 @@
+"""GPU parity of the decode GEMVs (qgemv_2bit, qgemv_nf4, qgemv_2bit_grouped)
+with the fp64 oracle: normwise relative error <= 1e-3 (fp32 accumulation,
+fp16 output), fp16 output == nearest-even of the fp32 output, and exact
+zeros for a zero input."""
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_weight_quantized_qw_amd import inputs, qw
+from gpu_util import TOL, norm_err, to_dev, f16_dev, oracle_2bit, oracle_nf4
+
+pytestmark = pytest.mark.gpu
+
+
+def _packed_2bit(W, idx=None):
+    idd = to_dev(np.asarray(idx, np.int32)) if idx is not None and len(idx) else None
+    return qw.qw_pack(to_dev(W), qw.QW_FMT_2BIT_G32, idd)
+
+
+def _run_2bit(pw, x16, f32=False):
+    import torch
+    y = qw.qgemv_2bit(pw, f16_dev(x16), out_dtype=torch.float32 if f32 else torch.float16)
+    return y.float().cpu().numpy()
+
+
+def _ref_2bit(W, x16, idx=None):
+    r = oracle.quantize_2bit(W, idx)
+    return oracle.gemv_2bit_ref(x16, r["q"], r["S"], r["Z"], r["idx"], r["W_O"])
+
+
+def test_gemv_2bit_single_layer_2048():
+    W = inputs.weight(2048, 2048, workload=1)
+    x = inputs.act_f16(1, 2048, workload=1)
+    pw = _packed_2bit(W)
+    ref = _ref_2bit(W, x)
+    y16 = _run_2bit(pw, x)
+    y32 = _run_2bit(pw, x, f32=True)
+    e = norm_err(y32, ref)
+    print(f"2048x2048 B=1 fp32-out err {e:.3e}, fp16-out err {norm_err(y16, ref):.3e}")
+    assert e <= TOL and norm_err(y16, ref) <= TOL
+    np.testing.assert_array_equal(y16.astype(np.float16), y32.astype(np.float16))
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 8])
+def test_gemv_2bit_14b_shape_with_anchors(B):
+    W = inputs.weight(13824, 5120, workload=3)
+    X = inputs.profile(256, 5120, workload=3)
+    idx = oracle.select_outliers(W, X, 0.035)
+    x = inputs.act_f16(B, 5120, workload=3)
+    pw = _packed_2bit(W, idx)
+    y = _run_2bit(pw, x)
+    e = norm_err(y, _ref_2bit(W, x, idx))
+    print(f"13824x5120 anchors=179 B={B} err {e:.3e}")
+    assert e <= TOL
+
+
+@pytest.mark.parametrize("N,K,n_anchor", [(1, 32, 0), (7, 96, 2), (33, 1056, 5), (130, 2080, 0),
+                                          (64, 3072, 40), (5, 27648, 967)])
+@pytest.mark.parametrize("B", [1, 2, 4])
+def test_gemv_2bit_ragged(N, K, n_anchor, B):
+    W = inputs.weight(N, K, workload=70)
+    idx = np.sort(np.random.default_rng(N * K).choice(K, n_anchor, replace=False)).astype(np.int32)
+    x = inputs.act_f16(B, K, workload=70)
+    pw = _packed_2bit(W, idx if n_anchor else None)
+    e = norm_err(_run_2bit(pw, x, f32=True), _ref_2bit(W, x, idx if n_anchor else None))
+    assert e <= TOL, e
+
+
+def test_gemv_2bit_zero_input_gives_zero():
+    W = inputs.weight(64, 512, workload=71)
+    pw = _packed_2bit(W, np.array([3, 300], np.int32))
+    y = _run_2bit(pw, np.zeros((2, 512), np.float16), f32=True)
+    assert np.all(y == 0.0)
+
+
+@pytest.mark.parametrize("scale", [1e-4, 1.0, 300.0, 3000.0, 60000.0])
+def test_gemv_2bit_input_scales(scale):
+    W = inputs.weight(256, 1024, workload=72)
+    x = (inputs.act_f16(2, 1024, workload=72).astype(np.float32) * scale)
+    x = np.clip(x, -65504, 65504).astype(np.float16)
+    pw = _packed_2bit(W)
+    e = norm_err(_run_2bit(pw, x, f32=True), _ref_2bit(W, x))
+    print(f"input scale {scale}: err {e:.3e}")
+    assert e <= TOL
+
+
+def test_gemv_2bit_one_hot_reads_columns():
+    W = inputs.weight(96, 256, workload=73)
+    idx = np.array([5, 200], np.int32)
+    pw = _packed_2bit(W, idx)
+    r = oracle.quantize_2bit(W, idx)
+    Wh = oracle.dequant_2bit(r["q"], r["S"], r["Z"])
+    for k in (0, 5, 17, 31, 32, 200, 255):
+        x = np.zeros((1, 256), np.float16)
+        x[0, k] = 1
+        y = _run_2bit(pw, x, f32=True)[0]
+        ref = r["W_O"][:, list(idx).index(k)].astype(np.float64) if k in idx else Wh[:, k]
+        assert norm_err(y, ref) <= 1e-6
+
+
+def test_gemv_2bit_grouped_equals_separate():
+    import torch
+    K = 5120
+    pws, xs = [], inputs.act_f16(1, K, workload=74)
+    for p, N in enumerate((5120, 1024, 1024)):
+        W = inputs.weight(N, K, workload=74, proj=p)
+        X = inputs.profile(64, K, workload=74, proj=p)
+        pws.append(_packed_2bit(W, oracle.select_outliers(W, X, 0.035)))
+    xd = f16_dev(xs)
+    ys = qw.qgemv_2bit_grouped(pws, xd, out_dtype=torch.float32)
+    for pw, yg in zip(pws, ys):
+        ysep = qw.qgemv_2bit(pw, xd, out_dtype=torch.float32)
+        np.testing.assert_array_equal(yg.cpu().numpy(), ysep.cpu().numpy())
+
+
+def _run_nf4(W, x16, f32=False):
+    import torch
+    pw = qw.qw_pack(to_dev(W), qw.QW_FMT_NF4_B64)
+    y = qw.qgemv_nf4(pw, f16_dev(x16), out_dtype=torch.float32 if f32 else torch.float16)
+    return y.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("B", [1, 2, 4, 8])
+def test_gemv_nf4_llama7b_mlp_shape(B):
+    W = inputs.weight(11008, 4096, workload=2)
+    x = inputs.act_f16(B, 4096, workload=2)
+    q, a = oracle.quantize_nf4(W)
+    ref = oracle.gemv_nf4_ref(x, q, a)
+    y16 = _run_nf4(W, x)
+    e = norm_err(y16, ref)
+    print(f"NF4 11008x4096 B={B} err {e:.3e}")
+    assert e <= TOL
+
+
+def test_gemv_2bit_llama7b_mlp_shape():
+    W = inputs.weight(11008, 4096, workload=2)
+    x = inputs.act_f16(1, 4096, workload=2)
+    pw = _packed_2bit(W)
+    e = norm_err(_run_2bit(pw, x), _ref_2bit(W, x))
+    assert e <= TOL
+
+
+@pytest.mark.parametrize("N,K", [(3, 64), (5, 192), (64, 4160), (9, 28672)])
+@pytest.mark.parametrize("B", [1, 3])
+def test_gemv_nf4_ragged(N, K, B):
+    W = inputs.weight(N, K, workload=75)
+    W[0, :64] = 0.0
+    x = inputs.act_f16(B, K, workload=75)
+    q, a = oracle.quantize_nf4(W)
+    e = norm_err(_run_nf4(W, x, f32=True), oracle.gemv_nf4_ref(x, q, a))
+    assert e <= TOL, e
+
+
+def test_gemv_nf4_fp16_out_is_rounded_fp32_out():
+    W = inputs.weight(512, 1024, workload=76)
+    x = inputs.act_f16(2, 1024, workload=76)
+    np.testing.assert_array_equal(_run_nf4(W, x).astype(np.float16),
+                                  _run_nf4(W, x, f32=True).astype(np.float16))

@@ -1,0 +1,122 @@
+"""CPU checks of the C ABI: libqw.so loads, exports every function that
+include/qw.h declares, its host-side constants agree with the oracle bit for
+bit (the two sides compute them independently), and argument validation
+returns the documented status before any device work. No kernel runs."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_weight_quantized_qw_amd import qw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(qw.LIB_PATH):
+        from bit_weight_quantized_qw_amd.build import build
+        build()
+    return qw.lib()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "qw.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(q\w+)\s*\(", src)) - {"qw_weight"})
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(names) == sorted(qw.EXPORTS)
+
+
+def test_abi_version_and_status_text(L):
+    assert qw.qw_abi_version() == 1
+    for s in range(6):
+        assert qw.qw_status_str(s)
+    assert qw.qw_status_str(99) == "unknown status"
+
+
+def test_codebook_matches_oracle(L):
+    np.testing.assert_array_equal(qw.qw_codebook_2bit(), oracle.CODEBOOK_F32)
+
+
+def test_nf4_levels_match_oracle_bit_exact(L):
+    a = qw.qw_nf4_levels().view(np.uint32)
+    b = oracle.nf4_levels().view(np.uint32)
+    np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("K,frac", [(5120, 0.035), (27648, 0.035), (2048, 0.0), (4096, 0.01), (100, 0.5)])
+def test_outlier_count_matches_oracle(L, K, frac):
+    assert qw.qw_outlier_count(K, frac) == oracle.outlier_count(K, frac)
+
+
+def test_outlier_count_rejects_bad_fraction(L):
+    assert qw.qw_outlier_count(100, 1.0) == -1
+    assert qw.qw_outlier_count(100, -0.1) == -1
+
+
+def test_packed_sizes(L):
+    assert qw.qw_packed_sizes(qw.QW_FMT_2BIT_G32, 13824, 5120, 179) == (
+        13824 * 1280, 13824 * 160 * 4, 13824 * 184 * 2, 184)
+    assert qw.qw_packed_sizes(qw.QW_FMT_NF4_B64, 11008, 4096, 0) == (
+        11008 * 2048, 11008 * 64 * 4, 0, 0)
+    for bad in [(qw.QW_FMT_2BIT_G32, 0, 64, 0), (qw.QW_FMT_2BIT_G32, 4, 48, 0),
+                (qw.QW_FMT_NF4_B64, 4, 96, 0), (qw.QW_FMT_NF4_B64, 4, 128, 3),
+                (qw.QW_FMT_2BIT_G32, 4, 64, 64), (7, 4, 64, 0)]:
+        with pytest.raises(qw.QwError) as e:
+            qw.qw_packed_sizes(*bad)
+        assert e.value.status == qw.QW_ERR_INVALID_ARG
+
+
+def _view(fmt, N, K, n_out=0, ptr=0x1000):
+    pad = (n_out + 7) // 8 * 8 if n_out else 0
+    return qw.qw_weight(fmt, N, K, n_out, pad, ptr, ptr, ptr if n_out else None, ptr if n_out else None)
+
+
+def test_validation_before_device_work(L):
+    s = ctypes.c_void_p(0)
+    v = _view(qw.QW_FMT_2BIT_G32, 16, 64)
+    p = ctypes.c_void_p(0x1000)
+    # NULL weight / wrong format / bad batch / bad dtype -> invalid argument
+    assert L.qgemv_2bit(None, p, 1, p, qw.QW_DT_F16, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qgemv_nf4(ctypes.byref(v), p, 1, p, qw.QW_DT_F16, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qgemv_2bit(ctypes.byref(v), p, 0, p, qw.QW_DT_F16, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qgemv_2bit(ctypes.byref(v), p, 9, p, qw.QW_DT_F16, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qgemv_2bit(ctypes.byref(v), p, 1, p, qw.QW_DT_BF16, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qgemm_prefill(ctypes.byref(v), p, 0, p, qw.QW_DT_BF16, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qgemm_prefill(ctypes.byref(v), p, 4, p, qw.QW_DT_F16, s) == qw.QW_ERR_INVALID_ARG
+    # misaligned pointers
+    odd = ctypes.c_void_p(0x1004)
+    assert L.qgemv_2bit(ctypes.byref(v), odd, 1, p, qw.QW_DT_F16, s) == qw.QW_ERR_ALIGNMENT
+    vb = _view(qw.QW_FMT_2BIT_G32, 16, 64, ptr=0x1008)
+    assert L.qw_pack(p, ctypes.byref(vb), s) == qw.QW_ERR_ALIGNMENT
+    # anchors declared without buffers
+    va = qw.qw_weight(qw.QW_FMT_2BIT_G32, 16, 64, 3, 8, 0x1000, 0x1000, None, None)
+    assert L.qgemv_2bit(ctypes.byref(va), p, 1, p, qw.QW_DT_F16, s) == qw.QW_ERR_INVALID_ARG
+    # prefill needs K % 64
+    v96 = _view(qw.QW_FMT_2BIT_G32, 16, 96)
+    assert L.qgemm_prefill(ctypes.byref(v96), p, 4, p, qw.QW_DT_F32, s) == qw.QW_ERR_UNSUPPORTED
+    # select_outliers: bad fraction / sizes
+    assert L.qw_select_outliers(p, 4, 64, p, 2, 1.5, 1, p, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_select_outliers(p, 4, 64, p, 0, 0.1, 1, p, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_select_outliers(p, 4, 64, p, 2, 0.1, 7, p, s) == qw.QW_ERR_INVALID_ARG
+
+
+def test_valid_call_without_gpu_reports_no_device(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    s = ctypes.c_void_p(0)
+    v = _view(qw.QW_FMT_2BIT_G32, 16, 64)
+    p = ctypes.c_void_p(0x1000)
+    assert L.qgemv_2bit(ctypes.byref(v), p, 1, p, qw.QW_DT_F16, s) == qw.QW_ERR_NO_DEVICE
