@@ -91,6 +91,23 @@ qw_status current_device(int *cu_count) {
   return QW_OK;
 }
 
+qw_status check_weight_view(const qw_weight *w, int format, int K_expect) {
+  if (!w || w->format != format) return QW_ERR_INVALID_ARG;
+  qw_sizes z;
+  qw_status st = qw_packed_sizes((qw_format)format, w->N, w->K, w->n_out, &z);
+  if (st != QW_OK) return st;
+  if (K_expect > 0 && w->K != K_expect) return QW_ERR_INVALID_ARG;
+  if (!w->codes || !w->scales) return QW_ERR_INVALID_ARG;
+  if (!aligned16(w->codes) || !aligned16(w->scales)) return QW_ERR_ALIGNMENT;
+  if (w->n_out > 0) {
+    if (!w->out_idx || !w->out_w || !w->out_mask) return QW_ERR_INVALID_ARG;
+    if (w->n_out_pad < z.n_out_pad || (w->n_out_pad & 7)) return QW_ERR_INVALID_ARG;
+    if (!aligned16(w->out_idx) || !aligned16(w->out_w) || !aligned16(w->out_mask))
+      return QW_ERR_ALIGNMENT;
+  }
+  return QW_OK;
+}
+
 }  // namespace qw
 
 extern "C" {
@@ -109,29 +126,27 @@ const char *qw_status_str(qw_status s) {
   return "unknown status";
 }
 
-qw_status qw_packed_sizes(qw_format fmt, int N, int K, int n_out,
-                          size_t *codes_bytes, size_t *scales_bytes,
-                          size_t *out_w_bytes, int *n_out_pad) {
-  if (N <= 0 || K <= 0 || n_out < 0 || n_out >= K) return QW_ERR_INVALID_ARG;
-  size_t c = 0, s = 0, o = 0;
-  int pad = 0;
+qw_status qw_packed_sizes(qw_format fmt, int N, int K, int n_out, qw_sizes *out) {
+  if (!out || N <= 0 || K <= 0 || n_out < 0 || n_out >= K) return QW_ERR_INVALID_ARG;
+  qw_sizes z{};
   if (fmt == QW_FMT_2BIT_G32) {
     if (K % 32) return QW_ERR_INVALID_ARG;
-    c = (size_t)N * (size_t)(K / 4);
-    s = (size_t)N * (size_t)(K / 32) * 4;
-    pad = n_out ? qw::pad8(n_out) : 0;
-    o = (size_t)N * (size_t)pad * 2;
+    z.codes = (size_t)N * (size_t)(K / 4);
+    z.scales = (size_t)N * (size_t)(K / 32) * 4;
+    if (n_out > 0) {
+      z.n_out_pad = qw::pad8(n_out);
+      z.out_idx = (size_t)n_out * 4;
+      z.out_w = (size_t)N * (size_t)z.n_out_pad * 2;
+      z.out_mask = (size_t)(K / 32) * 4;
+    }
   } else if (fmt == QW_FMT_NF4_B64) {
     if (K % 64 || n_out != 0) return QW_ERR_INVALID_ARG;
-    c = (size_t)N * (size_t)(K / 2);
-    s = (size_t)N * (size_t)(K / 64) * 4;
+    z.codes = (size_t)N * (size_t)(K / 2);
+    z.scales = (size_t)N * (size_t)(K / 64) * 4;
   } else {
     return QW_ERR_INVALID_ARG;
   }
-  if (codes_bytes) *codes_bytes = c;
-  if (scales_bytes) *scales_bytes = s;
-  if (out_w_bytes) *out_w_bytes = o;
-  if (n_out_pad) *n_out_pad = pad;
+  *out = z;
   return QW_OK;
 }
 

@@ -1,402 +1,104 @@
-// Decode GEMV against the adaptive non-uniform 2-bit code
-// ("On-The-Fly Weight Synthesizer (OTF-LLM Engine v4.0)": codebook of
-// section 2, per-group scale/offset of section 3, fp16 anchors of section 4,
-// four codes per byte and in-register decode from "Key v4.0 Innovations").
-//
-//   y[b][n] = sum_g S_g * sum_{k in g} x_R[b][k] C[q_k] + Z_g * X_g[b]
-//           + sum_o x[b][idx_o] W_O[n][o]
-//
-// Mapping: a workgroup owns a contiguous range of rows; its W waves split K.
-// Lane `l` of wave `w` owns the 16-code dwords u = (j*W + w)*64 + l of every
-// row (j < UW), so its slice of x is loaded once and kept in registers while
-// the workgroup walks its rows; all loads of a wave are contiguous.
-//
-// Decode without a lookup table: with q = l + 2h (low/high bit of the code),
-// C[q] = C0 + d1*l + d2*h exactly (d1 = C1-C0, d2 = C2-C0; C3-C0 = d1+d2 for
-// the symmetric codebook), so per 16 weights
-//   sum x C[q] = C0*X + d1*sum x q + (d2 - 2 d1)*sum x h.
-// A 2-bit field masked in place inside the 32-bit code word is a subnormal
-// fp16 (value q * 2^(2f-24) for the f-th field of each half-word), so one
-// v_and_b32 turns two fields -- element f and element f+8 of the dword --
-// into an fp16 pair that v_dot2_f32_f16 multiplies exactly with a pair of x
-// values. x is pre-scaled by 2^(s-2f) per field so every product lands on
-// the common scale 2^(s-24); fields 5..7 of each half are first shifted down
-// by 10 bits. s <= 8 is chosen per batch row from max|x| so nothing
-// overflows fp16; for |x| < 256 (always for N(0,1) inputs) every product is
-// exact and only fp32 accumulation rounds.
-#include "qw_internal.h"
+// Host side of the 2-bit decode GEMV: validation, work split, dispatch.
+// The kernel itself (and the decode scheme) is in gemv2_kernel.h.
+#include <stdlib.h>
+
+#include "gemv2_kernel.h"
 
 namespace qw {
+namespace gemv2 {
 namespace {
 
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-
-constexpr int kMaxMats = 4;
-
-struct Mat {
-  const uint32_t *codes;  // [N][K/16]
-  const uint32_t *sz;     // [N][K/32] : fp16 S | fp16 Z << 16
-  const int32_t *idx;     // [n_out]
-  const uint32_t *wo;     // [N][n_out_pad/2] fp16 pairs
-  void *y;                // [B][N]
-  int N, n_out, n_out_pad, wg_begin;
-};
-
-struct Args {
-  Mat m[kMaxMats];
-  int count;
-  const uint16_t *x;  // [B][K]
-  int K;
-  int rows_per_wg;
-};
-
-__device__ inline float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), c, false);
-}
-
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
-__device__ inline uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, off, 64));
-  return v;
-}
-
-// fp16 bits of 2^k for -14 <= k <= 15, replicated in both halves.
-__device__ inline uint32_t pow2_pair(int k) {
-  uint32_t h = (uint32_t)(k + 15) << 10;
-  return h | (h << 16);
-}
-
-__device__ inline uint32_t pk_mul(uint32_t a, uint32_t b) {
-  h2 r = __builtin_bit_cast(h2, a) * __builtin_bit_cast(h2, b);
-  return __builtin_bit_cast(uint32_t, r);
-}
-
-template <int B, int UW, bool F32OUT>
-__global__ __launch_bounds__(512) void gemv2_kernel(Args a) {
-  extern __shared__ uint32_t lds[];
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int W = blockDim.x >> 6;
-  const int T = blockDim.x;
-
-  // pick this workgroup's matrix with selects (no dynamic indexing of the
-  // argument block, which would go through scratch memory)
-  Mat M = a.m[0];
-#pragma unroll
-  for (int i = 1; i < kMaxMats; ++i)
-    if (i < a.count && (int)blockIdx.x >= a.m[i].wg_begin) M = a.m[i];
-  const int K = a.K;
-  const int KD = K >> 4;          // code dwords per row
-  const int KS = K >> 5;          // scale dwords per row
-  const int KA = M.n_out_pad >> 1; // anchor dwords per row
-  const int r0 = ((int)blockIdx.x - M.wg_begin) * a.rows_per_wg;
-  const int r1 = min(M.N, r0 + a.rows_per_wg);
-
-  // LDS: outlier bitmask [KS] | per-wave max [16*B] | x at anchors [B][n_out_pad]
-  //      | row partials [rows_per_wg][W][B]
-  uint32_t *omask = lds;
-  uint32_t *wmax = omask + KS;
-  uint16_t *xo = reinterpret_cast<uint16_t *>(wmax + 16 * B);
-  float *parts = reinterpret_cast<float *>(wmax + 16 * B + ((B * M.n_out_pad + 1) >> 1));
-
-  for (int i = threadIdx.x; i < KS; i += T) omask[i] = 0;
-  __syncthreads();
-  for (int o = threadIdx.x; o < M.n_out; o += T) {
-    const int c = M.idx[o];
-    if (c >= 0 && c < K) atomicOr(&omask[c >> 5], 1u << (c & 31));
-  }
-  for (int i = threadIdx.x; i < B * M.n_out_pad; i += T) {
-    const int b = i / M.n_out_pad, o = i - b * M.n_out_pad;
-    const int c = (o < M.n_out) ? M.idx[o] : -1;
-    xo[i] = (c >= 0 && c < K) ? a.x[(size_t)b * K + c] : (uint16_t)0;
-  }
-  __syncthreads();
-
-  // Load this lane's x slice (raw fp16 pairs), zero anchor channels, and
-  // find max |x_R| per batch row.
-  uint32_t xr[UW][B][8];
-  uint32_t mx[B];
-#pragma unroll
-  for (int b = 0; b < B; ++b) mx[b] = 0;
-#pragma unroll
-  for (int j = 0; j < UW; ++j) {
-    const int u = (j * W + w) * 64 + lane;
-    const bool ok = u < KD;
-    const uint32_t om = ok ? (omask[u >> 1] >> ((u & 1) * 16)) & 0xFFFFu : 0u;
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      uint4 v0 = make_uint4(0, 0, 0, 0), v1 = make_uint4(0, 0, 0, 0);
-      if (ok) {
-        const uint4 *xp = reinterpret_cast<const uint4 *>(a.x + (size_t)b * K + (size_t)u * 16);
-        v0 = xp[0];
-        v1 = xp[1];
-      }
-      uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      if (om) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          uint32_t keep = (((om >> (2 * i)) & 1u) ? 0u : 0xFFFFu) |
-                          (((om >> (2 * i + 1)) & 1u) ? 0u : 0xFFFF0000u);
-          d[i] &= keep;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        xr[j][b][i] = d[i];
-        mx[b] = max(mx[b], max(d[i] & 0x7FFFu, (d[i] >> 16) & 0x7FFFu));
-      }
-    }
-  }
-#pragma unroll
-  for (int b = 0; b < B; ++b) {
-    const uint32_t m = wave_max_u32(mx[b]);
-    if (lane == 0) wmax[w * B + b] = m;
-  }
-  __syncthreads();
-  int s[B];
-#pragma unroll
-  for (int b = 0; b < B; ++b) {
-    uint32_t m = 0;
-    for (int i = 0; i < W; ++i) m = max(m, wmax[i * B + b]);
-    const int e5 = (int)(m >> 10);
-    s[b] = (e5 == 0) ? 8 : min(8, 30 - e5);
-  }
-
-  // Pre-scaled pairs (x[f], x[f+8]) per field, group sums, coefficients.
-  uint32_t xp[UW][B][8];
-  float Xh[UW][B], CX[UW][B];
-  float e1[B], e2[B];
-  const float C0 = -1.52f, d1 = -0.45f - C0, d2 = 0.45f - C0;
-#pragma unroll
-  for (int b = 0; b < B; ++b) {
-    e1[b] = d1 * __builtin_ldexpf(1.0f, 24 - s[b]);
-    e2[b] = (d2 - 2.0f * d1) * __builtin_ldexpf(1.0f, 23 - s[b]);
-  }
-#pragma unroll
-  for (int j = 0; j < UW; ++j) {
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-      float xs = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xs = dot2(xr[j][b][i], 0x3C003C00u, xs);
-      Xh[j][b] = xs;
-      CX[j][b] = C0 * xs;
-#pragma unroll
-      for (int f = 0; f < 8; ++f) {
-        const uint32_t lo = xr[j][b][f >> 1], hi = xr[j][b][4 + (f >> 1)];
-        const uint32_t pair = __builtin_amdgcn_perm(hi, lo, (f & 1) ? 0x07060302u : 0x05040100u);
-        const int fp = (f < 5) ? f : f - 5;
-        xp[j][b][f] = pk_mul(pair, pow2_pair(s[b] - 2 * fp));
-      }
-    }
-  }
-
-  constexpr int RU = (UW <= 2) ? 4 : 2;
-  for (int r = r0; r < r1; r += RU) {
-    uint32_t cw[RU][UW], sw[RU][UW];
-#pragma unroll
-    for (int i = 0; i < RU; ++i) {
-      const int rr = r + i;
-#pragma unroll
-      for (int j = 0; j < UW; ++j) {
-        const int u = (j * W + w) * 64 + lane;
-        const bool ok = rr < r1 && u < KD;
-        cw[i][j] = ok ? __builtin_nontemporal_load(M.codes + (size_t)rr * KD + u) : 0u;
-        sw[i][j] = ok ? __builtin_nontemporal_load(M.sz + (size_t)rr * KS + (u >> 1)) : 0u;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < RU; ++i) {
-      const int rr = r + i;
-      if (rr >= r1) break;
-      float acc[B];
-#pragma unroll
-      for (int b = 0; b < B; ++b) acc[b] = 0.0f;
-#pragma unroll
-      for (int j = 0; j < UW; ++j) {
-        const uint32_t c = cw[i][j];
-        const uint32_t c2 = c >> 10;
-        uint32_t mq[8], mh[8];
-#pragma unroll
-        for (int f = 0; f < 5; ++f) {
-          mq[f] = c & (0x00030003u << (2 * f));
-          mh[f] = c & (0x00020002u << (2 * f));
-        }
-#pragma unroll
-        for (int f = 5; f < 8; ++f) {
-          mq[f] = c2 & (0x00030003u << (2 * (f - 5)));
-          mh[f] = c2 & (0x00020002u << (2 * (f - 5)));
-        }
-        const float S = f16_bits_to_f32((uint16_t)(sw[i][j] & 0xFFFFu));
-        const float Z = f16_bits_to_f32((uint16_t)(sw[i][j] >> 16));
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-          float aq = 0.0f, ah = 0.0f;
-#pragma unroll
-          for (int f = 0; f < 8; ++f) {
-            aq = dot2(xp[j][b][f], mq[f], aq);
-            ah = dot2(xp[j][b][f], mh[f], ah);
-          }
-          float t = __builtin_fmaf(e1[b], aq, CX[j][b]);
-          t = __builtin_fmaf(e2[b], ah, t);
-          acc[b] = __builtin_fmaf(S, t, acc[b]);
-          acc[b] = __builtin_fmaf(Z, Xh[j][b], acc[b]);
-        }
-      }
-      // fp16 anchors: exact fp16 products, fp32 accumulation
-      for (int ad = w * 64 + lane; ad < KA; ad += W * 64) {
-        const uint32_t wv = M.wo[(size_t)rr * KA + ad];
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-          const uint32_t xv = reinterpret_cast<const uint32_t *>(xo + b * M.n_out_pad)[ad];
-          acc[b] = dot2(xv, wv, acc[b]);
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const float v = wave_sum(acc[b]);
-        if (lane == 0) parts[((rr - r0) * W + w) * B + b] = v;
-      }
-    }
-  }
-  __syncthreads();
-  const int nrows = r1 - r0;
-  for (int t = threadIdx.x; t < nrows * B; t += T) {
-    const int rl = t / B, b = t - rl * B;
-    float v = 0.0f;
-    for (int i = 0; i < W; ++i) v += parts[(rl * W + i) * B + b];
-    const size_t o = (size_t)b * M.N + (r0 + rl);
-    if (F32OUT) {
-      reinterpret_cast<float *>(M.y)[o] = v;
-    } else {
-      reinterpret_cast<_Float16 *>(M.y)[o] = (_Float16)v;
-    }
-  }
-}
-
-template <int B, int UW>
-qw_status launch_uw(const Args &a, bool f32, int W, int grid, size_t lds, hipStream_t s) {
-  if (f32)
-    gemv2_kernel<B, UW, true><<<grid, W * 64, lds, s>>>(a);
-  else
-    gemv2_kernel<B, UW, false><<<grid, W * 64, lds, s>>>(a);
-  QW_LAUNCH_CHECK();
-  return QW_OK;
-}
-
-template <int B>
-qw_status launch_b(const Args &a, bool f32, int UW, int W, int grid, size_t lds, hipStream_t s) {
-  if constexpr (B == 1) {
-    switch (UW) {
-      case 1: return launch_uw<1, 1>(a, f32, W, grid, lds, s);
-      case 2: return launch_uw<1, 2>(a, f32, W, grid, lds, s);
-      case 3: return launch_uw<1, 3>(a, f32, W, grid, lds, s);
-      case 4: return launch_uw<1, 4>(a, f32, W, grid, lds, s);
-      case 5: return launch_uw<1, 5>(a, f32, W, grid, lds, s);
-      case 6: return launch_uw<1, 6>(a, f32, W, grid, lds, s);
-      case 7: return launch_uw<1, 7>(a, f32, W, grid, lds, s);
-      default: return launch_uw<1, 8>(a, f32, W, grid, lds, s);
-    }
-  } else {
-    switch (UW) {
-      case 1: return launch_uw<B, 1>(a, f32, W, grid, lds, s);
-      case 2: return launch_uw<B, 2>(a, f32, W, grid, lds, s);
-      case 3: return launch_uw<B, 3>(a, f32, W, grid, lds, s);
-      default: return launch_uw<B, 4>(a, f32, W, grid, lds, s);
-    }
-  }
-}
-
-int max_uw(int B) { return B == 1 ? 8 : 4; }
-
-qw_status check_weight(const qw_weight *w, int K_expect) {
-  if (!w || w->format != QW_FMT_2BIT_G32) return QW_ERR_INVALID_ARG;
-  size_t cb, sb, ob;
-  int pad;
-  qw_status st = qw_packed_sizes(QW_FMT_2BIT_G32, w->N, w->K, w->n_out, &cb, &sb, &ob, &pad);
-  if (st != QW_OK) return st;
-  if (K_expect > 0 && w->K != K_expect) return QW_ERR_INVALID_ARG;
-  if (!w->codes || !w->scales) return QW_ERR_INVALID_ARG;
-  if (!aligned16(w->codes) || !aligned16(w->scales)) return QW_ERR_ALIGNMENT;
-  if (w->n_out > 0) {
-    if (!w->out_idx || !w->out_w || w->n_out_pad < pad || (w->n_out_pad & 7)) return QW_ERR_INVALID_ARG;
-    if (!aligned16(w->out_idx) || !aligned16(w->out_w)) return QW_ERR_ALIGNMENT;
-  }
-  return QW_OK;
-}
+int max_uw(int B) { return B == 1 ? 8 : (B == 2 ? 3 : 2); }
 
 int env_int(const char *name, int dflt) {
   const char *v = getenv(name);
   return v ? atoi(v) : dflt;
 }
 
-// One launch for batch width Bk in {1, 2, 4}; x and the y pointers already
-// point at the first batch row of this slice; y rows keep stride N.
-qw_status gemv2_launch_slice(const qw_weight *ws, int count, const uint16_t *x, int Bk,
-                             void *const *ys, bool f32, int cus, hipStream_t s) {
+// Launch geometry for one batch slice of width Bk.
+struct Plan {
+  int W, UW, UA, threads, grid;
+  size_t lds;
+};
+
+// Returns false when this width does not fit (waves or LDS).
+bool plan_slice(const qw_weight *ws, int count, int Bk, int cus, Plan *p, int *rows_per_wg_out,
+                int *wg_begin_out) {
   const int K = ws[0].K;
   const int KD = K / 16;
   const int U = (KD + 63) / 64;  // 64-lane dword iterations per row
   const int W = (U + max_uw(Bk) - 1) / max_uw(Bk);
-  if (W > 8) return QW_ERR_UNSUPPORTED;
+  if (W > kMaxWaves) return false;
   const int UW = (U + W - 1) / W;
-
   long total_rows = 0;
-  int max_pad = 0;
+  int ka_max = 0;
   for (int i = 0; i < count; ++i) {
     total_rows += ws[i].N;
-    max_pad = max(max_pad, ws[i].n_out > 0 ? ws[i].n_out_pad : 0);
+    if (ws[i].n_out > 0) ka_max = max(ka_max, ws[i].n_out_pad / 2);
   }
-  int rpw = env_int("QW_GEMV_ROWS_PER_WG", 0);
-  if (rpw <= 0) {
-    const long target_waves = (long)cus * 16;
-    rpw = (int)((total_rows * W + target_waves - 1) / target_waves);
-    rpw = max(2, min(rpw, 32));
+  const int ua_need = (ka_max + 64 * W - 1) / (64 * W);
+  if (ua_need > 4) return false;
+  const int UA = ua_need == 0 ? 0 : (ua_need <= 2 ? 2 : 4);
+  const int V = kMaxWaves / W;
+  const int threads = 64 * W * V;
+  const long target_wgs = max(1L, (long)cus * env_int("QW_GEMV_WG_PER_CU", 1));
+  int rpg = env_int("QW_GEMV_ROWS_PER_WG", 0);
+  if (rpg <= 0) rpg = (int)max(1L, (total_rows + target_wgs - 1) / target_wgs);
+  int grid = 0;
+  for (int i = 0; i < count; ++i) {
+    wg_begin_out[i] = grid;
+    rows_per_wg_out[i] = rpg;
+    grid += (ws[i].N + rpg - 1) / rpg;
   }
+  const size_t lds = lds_bytes(Bk, K, rpg, W);
+  if (lds > 160 * 1024) return false;
+  const int xu = Bk == 1 ? x_units_per_thread<1>() : (Bk == 2 ? x_units_per_thread<2>()
+                                                              : x_units_per_thread<4>());
+  if (KD > xu * threads) return false;
+  *p = Plan{W, UW, UA, threads, grid, lds};
+  return true;
+}
 
+// One launch for batch width Bk in {1, 2, 4}; x and ys already point at the
+// first batch row of this slice (rows keep stride K and N).
+qw_status launch_slice(const qw_weight *ws, int count, const uint16_t *x, int Bk,
+                       void *const *ys, bool f32, const Plan &p, const int *rows_per_wg,
+                       const int *wg_begin, hipStream_t s) {
   Args a{};
   a.count = count;
   a.x = x;
-  a.K = K;
-  a.rows_per_wg = rpw;
-  int grid = 0;
+  a.K = ws[0].K;
+  a.W = p.W;
+  a.f32out = f32 ? 1 : 0;
   for (int i = 0; i < count; ++i) {
     Mat &m = a.m[i];
     m.codes = reinterpret_cast<const uint32_t *>(ws[i].codes);
     m.sz = reinterpret_cast<const uint32_t *>(ws[i].scales);
+    m.mask = ws[i].n_out > 0 ? ws[i].out_mask : nullptr;
     m.idx = ws[i].out_idx;
     m.wo = reinterpret_cast<const uint32_t *>(ws[i].out_w);
     m.y = ys[i];
     m.N = ws[i].N;
     m.n_out = ws[i].n_out;
     m.n_out_pad = ws[i].n_out > 0 ? ws[i].n_out_pad : 0;
-    m.wg_begin = grid;
-    grid += (m.N + rpw - 1) / rpw;
+    m.wg_begin = wg_begin[i];
+    m.rows_per_wg = rows_per_wg[i];
   }
-  const size_t lds = 4 * ((size_t)(K / 32) + 16 * Bk + (size_t)((Bk * max_pad + 1) / 2) +
-                          (size_t)rpw * W * Bk);
-  if (lds > 64 * 1024) return QW_ERR_UNSUPPORTED;
   switch (Bk) {
-    case 1: return launch_b<1>(a, f32, UW, W, grid, lds, s);
-    case 2: return launch_b<2>(a, f32, UW, W, grid, lds, s);
-    default: return launch_b<4>(a, f32, UW, W, grid, lds, s);
+    case 1: return launch_b1(a, p.UW, p.UA, p.grid, p.threads, p.lds, s);
+    case 2: return launch_b2(a, p.UW, p.UA, p.grid, p.threads, p.lds, s);
+    default: return launch_b4(a, p.UW, p.UA, p.grid, p.threads, p.lds, s);
   }
 }
 
-qw_status gemv2_launch(const qw_weight *ws, int count, const void *x, int B,
-                       void *const *ys, qw_dtype dt, hipStream_t s) {
+qw_status launch(const qw_weight *ws, int count, const void *x, int B, void *const *ys,
+                 qw_dtype dt, hipStream_t s) {
   if (!ws || count < 1 || count > kMaxMats || !x || !ys) return QW_ERR_INVALID_ARG;
   if (B < 1 || B > 8) return QW_ERR_INVALID_ARG;
   if (dt != QW_DT_F16 && dt != QW_DT_F32) return QW_ERR_INVALID_ARG;
   const int K = ws[0].K;
   for (int i = 0; i < count; ++i) {
-    qw_status st = check_weight(&ws[i], K);
+    qw_status st = check_weight_view(&ws[i], QW_FMT_2BIT_G32, K);
     if (st != QW_OK) return st;
     if (!ys[i]) return QW_ERR_INVALID_ARG;
     if (!aligned16(ys[i])) return QW_ERR_ALIGNMENT;
@@ -407,16 +109,27 @@ qw_status gemv2_launch(const qw_weight *ws, int count, const void *x, int B,
   if (st != QW_OK) return st;
   const bool f32 = dt == QW_DT_F32;
   const size_t esz = f32 ? 4 : 2;
-  // batch rows go through kernels of width 4, 2 and 1 (e.g. 7 = 4 + 2 + 1)
+  for (int i = 0; i < count; ++i) {
+    // buffer offsets are 32-bit
+    if ((size_t)ws[i].N * (ws[i].K / 4) >= (1ull << 31)) return QW_ERR_UNSUPPORTED;
+  }
+  // batch rows go through kernels of width 4, 2 and 1 (e.g. 7 = 4 + 2 + 1),
+  // narrower when the x slice of a wider one does not fit
   int b0 = 0;
   while (b0 < B) {
     const int rest = B - b0;
-    const int Bk = rest >= 4 ? 4 : (rest >= 2 ? 2 : 1);
+    int Bk = rest >= 4 ? 4 : (rest >= 2 ? 2 : 1);
+    Plan p;
+    int rpg[kMaxMats], wgb[kMaxMats];
+    while (!plan_slice(ws, count, Bk, cus, &p, rpg, wgb)) {
+      if (Bk == 1) return QW_ERR_UNSUPPORTED;
+      Bk >>= 1;
+    }
     void *ysl[kMaxMats];
     for (int i = 0; i < count; ++i)
       ysl[i] = reinterpret_cast<char *>(ys[i]) + (size_t)b0 * ws[i].N * esz;
-    st = gemv2_launch_slice(ws, count, reinterpret_cast<const uint16_t *>(x) + (size_t)b0 * K,
-                            Bk, ysl, f32, cus, s);
+    st = launch_slice(ws, count, reinterpret_cast<const uint16_t *>(x) + (size_t)b0 * K, Bk, ysl,
+                      f32, p, rpg, wgb, s);
     if (st != QW_OK) return st;
     b0 += Bk;
   }
@@ -424,6 +137,7 @@ qw_status gemv2_launch(const qw_weight *ws, int count, const void *x, int B,
 }
 
 }  // namespace
+}  // namespace gemv2
 }  // namespace qw
 
 extern "C" {
@@ -431,13 +145,12 @@ extern "C" {
 qw_status qgemv_2bit(const qw_weight *w, const void *x, int B, void *y, qw_dtype y_dtype,
                      void *stream) {
   void *ys[1] = {y};
-  return qw::gemv2_launch(w, 1, x, B, ys, y_dtype, qw::as_stream(stream));
+  return qw::gemv2::launch(w, 1, x, B, ys, y_dtype, qw::as_stream(stream));
 }
 
 qw_status qgemv_2bit_grouped(const qw_weight *ws, int count, const void *x, int B,
                              void *const *ys, qw_dtype y_dtype, void *stream) {
-  if (!ws) return QW_ERR_INVALID_ARG;
-  return qw::gemv2_launch(ws, count, x, B, ys, y_dtype, qw::as_stream(stream));
+  return qw::gemv2::launch(ws, count, x, B, ys, y_dtype, qw::as_stream(stream));
 }
 
 }  // extern "C"

@@ -4,15 +4,20 @@
 //
 //   y[b][n] = sum_blk absmax[n][blk] * sum_{k in blk} x[b][k] L[q_k]
 //
-// Same mapping as the 2-bit GEMV: a workgroup owns a row range, its waves
-// split K, lane `l` of wave `w` owns code dwords u = (j*W + w)*64 + l (8
-// codes each) and keeps those x pairs in registers across rows.
+// Work split as in the 2-bit GEMV: a workgroup owns a block of rows; workers
+// of W waves walk sub-ranges and split K; lane l of wave w owns code dwords
+// u = (j*W + w)*64 + l (8 codes each) and keeps those x pairs in registers
+// (copied once per workgroup through LDS). Weights come in through buffer
+// loads; the first 2*RU rows are requested before anything else, then rows
+// stream through two register buffers.
 //
 // Decode: each code byte (two elements) indexes a 256-entry LDS table whose
 // entry holds the pair (L[lo], L[hi]) split into an fp16 high part and an
 // fp16 remainder (L = hi + lo to within 2^-22 relative), so one ds_read_b64
 // feeds two v_dot2_f32_f16 for two weights with exact products and fp32
 // accumulation.
+#include <stdlib.h>
+
 #include "qw_internal.h"
 
 namespace qw {
@@ -27,7 +32,7 @@ struct ArgsNf4 {
   const float *absmax;    // [N][K/64]
   const uint16_t *x;      // [B][K]
   void *y;                // [B][N]
-  int N, K, rows_per_wg;
+  int N, K, rows_per_wg, W, f32out;
   Nf4Split L;
 };
 
@@ -35,27 +40,84 @@ __device__ inline float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), c, false);
 }
 
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+template <int CTRL, int ROW_MASK>
+__device__ inline float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                CTRL, ROW_MASK, 0xF, false));
+}
+
+__device__ inline float wave_sum_to_lane63(float v) {
+  v += dpp_f<0xB1, 0xF>(v);
+  v += dpp_f<0x4E, 0xF>(v);
+  v += dpp_f<0x124, 0xF>(v);
+  v += dpp_f<0x128, 0xF>(v);
+  v += dpp_f<0x142, 0xA>(v);
+  v += dpp_f<0x143, 0xC>(v);
   return v;
 }
 
-template <int B, int UW, bool F32OUT>
-__global__ __launch_bounds__(512) void gemv_nf4_kernel(ArgsNf4 a) {
-  extern __shared__ uint32_t lds[];
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int W = blockDim.x >> 6;
-  const int T = blockDim.x;
-  const int K = a.K;
-  const int KD = K >> 3;   // code dwords per row
-  const int KB = K >> 6;   // absmax per row
-  const int r0 = (int)blockIdx.x * a.rows_per_wg;
-  const int r1 = min(a.N, r0 + a.rows_per_wg);
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
 
-  uint2 *table = reinterpret_cast<uint2 *>(lds);         // [256]
-  float *parts = reinterpret_cast<float *>(lds + 512);    // [rows][W][B]
+__device__ inline uint32_t bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+
+constexpr uint32_t kOob = 0x7FFFFFF0u;
+
+// LDS: table uint2 [256] | x uint32 [B][K/2] | parts float [rows_per_wg][W][B]
+template <int B, int UW>
+__global__ __launch_bounds__(512) void gemv_nf4_kernel(ArgsNf4 a) {
+  constexpr int RU0 = (B == 1 ? 48 : 24) / (2 * UW);
+  constexpr int RU = RU0 < 1 ? 1 : (RU0 > 8 ? 8 : RU0);
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+  uint2 *table = reinterpret_cast<uint2 *>(lds);
+  uint32_t *xl = lds + 512;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
+  const int T = blockDim.x;
+  const int W = a.W;
+  const int V = (T >> 6) / W;
+  const int w = wave % W;
+  const int K = a.K;
+  const int KD = K >> 3;   // code dwords per row (8 codes each)
+  const int KB = K >> 6;   // absmax per row
+  float *parts = reinterpret_cast<float *>(xl + B * (K >> 1));
+  const int g0 = (int)blockIdx.x * a.rows_per_wg;
+  const int g1 = min(a.N, g0 + a.rows_per_wg);
+  const int rpw = (a.rows_per_wg + V - 1) / V;
+  const int r0 = min(g1, g0 + (wave / W) * rpw);
+  const int r1 = min(g1, r0 + rpw);
+
+  const auto rc = make_rsrc(a.codes, (uint32_t)((size_t)a.N * KD * 4));
+  const auto rm = make_rsrc(a.absmax, (uint32_t)((size_t)a.N * KB * 4));
+  uint32_t vc[UW], vm[UW];
+#pragma unroll
+  for (int j = 0; j < UW; ++j) {
+    const int u = (j * W + w) * 64 + lane;
+    vc[j] = u < KD ? (uint32_t)u * 4 : kOob;
+    vm[j] = u < KD ? (uint32_t)(u >> 3) * 4 : kOob;
+  }
+  uint32_t cA[RU][UW], cB[RU][UW], mA[RU][UW], mB[RU][UW];
+  auto load = [&](uint32_t (&c)[RU][UW], uint32_t (&m)[RU][UW], int rb) {
+#pragma unroll
+    for (int i = 0; i < RU; ++i) {
+      const int rr = rb + i;
+      if (rr < r1) {
+        const uint32_t so_c = (uint32_t)rr * KD * 4, so_m = (uint32_t)rr * KB * 4;
+#pragma unroll
+        for (int j = 0; j < UW; ++j) {
+          c[i][j] = bload(rc, vc[j], so_c);
+          m[i][j] = bload(rm, vm[j], so_m);
+        }
+      }
+    }
+  };
+  load(cA, mA, r0);
+  load(cB, mB, r0 + RU);
+
+  // level-pair table and this group's copy of x
   for (int v = threadIdx.x; v < 256; v += T) {
     const int q0 = v & 15, q1 = v >> 4;
     uint2 e;
@@ -63,51 +125,42 @@ __global__ __launch_bounds__(512) void gemv_nf4_kernel(ArgsNf4 a) {
     e.y = (uint32_t)a.L.lo[q0] | ((uint32_t)a.L.lo[q1] << 16);
     table[v] = e;
   }
+  for (int i = threadIdx.x; i < B * KD; i += T) {
+    const int b = i / KD, u = i - b * KD;
+    reinterpret_cast<uint4 *>(xl)[i] =
+        *reinterpret_cast<const uint4 *>(a.x + (size_t)b * K + (size_t)u * 8);
+  }
+  __syncthreads();
 
   uint32_t xr[UW][B][4];
 #pragma unroll
   for (int j = 0; j < UW; ++j) {
     const int u = (j * W + w) * 64 + lane;
-    const bool ok = u < KD;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (ok) v = *reinterpret_cast<const uint4 *>(a.x + (size_t)b * K + (size_t)u * 8);
+      if (u < KD) v = reinterpret_cast<const uint4 *>(xl)[b * KD + u];
       xr[j][b][0] = v.x; xr[j][b][1] = v.y; xr[j][b][2] = v.z; xr[j][b][3] = v.w;
     }
   }
-  __syncthreads();
 
-  constexpr int RU = (UW <= 4) ? 4 : 2;
-  for (int r = r0; r < r1; r += RU) {
-    uint32_t cw[RU][UW];
-    float am[RU][UW];
+  auto compute = [&](const uint32_t (&c)[RU][UW], const uint32_t (&m)[RU][UW], int rb) {
 #pragma unroll
     for (int i = 0; i < RU; ++i) {
-      const int rr = r + i;
-#pragma unroll
-      for (int j = 0; j < UW; ++j) {
-        const int u = (j * W + w) * 64 + lane;
-        const bool ok = rr < r1 && u < KD;
-        cw[i][j] = ok ? __builtin_nontemporal_load(a.codes + (size_t)rr * KD + u) : 0u;
-        am[i][j] = ok ? __builtin_nontemporal_load(a.absmax + (size_t)rr * KB + (u >> 3)) : 0.0f;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < RU; ++i) {
-      const int rr = r + i;
+      const int rr = rb + i;
       if (rr >= r1) break;
       float acc[B];
 #pragma unroll
       for (int b = 0; b < B; ++b) acc[b] = 0.0f;
 #pragma unroll
       for (int j = 0; j < UW; ++j) {
-        const uint32_t c = cw[i][j];
+        const uint32_t cw = c[i][j];
         uint2 e[4];
-        e[0] = table[c & 0xFFu];
-        e[1] = table[(c >> 8) & 0xFFu];
-        e[2] = table[(c >> 16) & 0xFFu];
-        e[3] = table[c >> 24];
+        e[0] = table[cw & 0xFFu];
+        e[1] = table[(cw >> 8) & 0xFFu];
+        e[2] = table[(cw >> 16) & 0xFFu];
+        e[3] = table[cw >> 24];
+        const float am = __builtin_bit_cast(float, m[i][j]);
 #pragma unroll
         for (int b = 0; b < B; ++b) {
           float t = 0.0f;
@@ -116,61 +169,81 @@ __global__ __launch_bounds__(512) void gemv_nf4_kernel(ArgsNf4 a) {
             t = dot2(xr[j][b][p], e[p].x, t);
             t = dot2(xr[j][b][p], e[p].y, t);
           }
-          acc[b] = __builtin_fmaf(am[i][j], t, acc[b]);
+          acc[b] = __builtin_fmaf(am, t, acc[b]);
         }
       }
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        const float v = wave_sum(acc[b]);
-        if (lane == 0) parts[((rr - r0) * W + w) * B + b] = v;
+        const float v = wave_sum_to_lane63(acc[b]);
+        if (lane == 63) {
+          if (W == 1) {
+            const size_t off = (size_t)b * a.N + rr;
+            if (a.f32out)
+              reinterpret_cast<float *>(a.y)[off] = v;
+            else
+              reinterpret_cast<_Float16 *>(a.y)[off] = (_Float16)v;
+          } else {
+            parts[((rr - g0) * W + w) * B + b] = v;
+          }
+        }
       }
     }
+  };
+
+  for (int r = r0; r < r1; r += 2 * RU) {
+    compute(cA, mA, r);
+    load(cA, mA, r + 2 * RU);
+    compute(cB, mB, r + RU);
+    load(cB, mB, r + 3 * RU);
   }
-  __syncthreads();
-  const int nrows = r1 - r0;
-  for (int t = threadIdx.x; t < nrows * B; t += T) {
-    const int rl = t / B, b = t - rl * B;
-    float v = 0.0f;
-    for (int i = 0; i < W; ++i) v += parts[(rl * W + i) * B + b];
-    const size_t o = (size_t)b * a.N + (r0 + rl);
-    if (F32OUT)
-      reinterpret_cast<float *>(a.y)[o] = v;
-    else
-      reinterpret_cast<_Float16 *>(a.y)[o] = (_Float16)v;
+
+  if (W > 1) {
+    __syncthreads();
+    const int nrows = g1 - g0;
+    for (int t = threadIdx.x; t < nrows * B; t += T) {
+      const int rl = t / B, b = t - rl * B;
+      float v = 0.0f;
+      for (int i = 0; i < W; ++i) v += parts[(rl * W + i) * B + b];
+      const size_t off = (size_t)b * a.N + (g0 + rl);
+      if (a.f32out)
+        reinterpret_cast<float *>(a.y)[off] = v;
+      else
+        reinterpret_cast<_Float16 *>(a.y)[off] = (_Float16)v;
+    }
   }
 }
 
 template <int B, int UW>
-qw_status launch_uw(const ArgsNf4 &a, bool f32, int W, int grid, size_t lds, hipStream_t s) {
-  if (f32)
-    gemv_nf4_kernel<B, UW, true><<<grid, W * 64, lds, s>>>(a);
-  else
-    gemv_nf4_kernel<B, UW, false><<<grid, W * 64, lds, s>>>(a);
+qw_status launch_uw(const ArgsNf4 &a, int grid, int threads, size_t lds, hipStream_t s) {
+  if (lds > 64 * 1024) {
+    QW_HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_nf4_kernel<B, UW>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+  }
+  gemv_nf4_kernel<B, UW><<<grid, threads, lds, s>>>(a);
   QW_LAUNCH_CHECK();
   return QW_OK;
 }
 
 template <int B>
-qw_status launch_b(const ArgsNf4 &a, bool f32, int UW, int W, int grid, size_t lds, hipStream_t s) {
+qw_status launch_b(const ArgsNf4 &a, int UW, int grid, int threads, size_t lds, hipStream_t s) {
   if constexpr (B == 1) {
-    switch (UW) {
-      case 1: return launch_uw<1, 1>(a, f32, W, grid, lds, s);
-      case 2: return launch_uw<1, 2>(a, f32, W, grid, lds, s);
-      case 3: return launch_uw<1, 3>(a, f32, W, grid, lds, s);
-      case 4: return launch_uw<1, 4>(a, f32, W, grid, lds, s);
-      case 6: return launch_uw<1, 6>(a, f32, W, grid, lds, s);
-      case 8: return launch_uw<1, 8>(a, f32, W, grid, lds, s);
-      case 5: case 7: return launch_uw<1, 8>(a, f32, W, grid, lds, s);
-      case 12: return launch_uw<1, 12>(a, f32, W, grid, lds, s);
-      default: return launch_uw<1, 16>(a, f32, W, grid, lds, s);
-    }
+    if (UW <= 1) return launch_uw<1, 1>(a, grid, threads, lds, s);
+    if (UW <= 2) return launch_uw<1, 2>(a, grid, threads, lds, s);
+    if (UW <= 4) return launch_uw<1, 4>(a, grid, threads, lds, s);
+    if (UW <= 6) return launch_uw<1, 6>(a, grid, threads, lds, s);
+    if (UW <= 8) return launch_uw<1, 8>(a, grid, threads, lds, s);
+    if (UW <= 12) return launch_uw<1, 12>(a, grid, threads, lds, s);
+    return launch_uw<1, 16>(a, grid, threads, lds, s);
+  } else if constexpr (B == 2) {
+    if (UW <= 1) return launch_uw<2, 1>(a, grid, threads, lds, s);
+    if (UW <= 2) return launch_uw<2, 2>(a, grid, threads, lds, s);
+    if (UW <= 4) return launch_uw<2, 4>(a, grid, threads, lds, s);
+    if (UW <= 6) return launch_uw<2, 6>(a, grid, threads, lds, s);
+    return launch_uw<2, 8>(a, grid, threads, lds, s);
   } else {
-    switch (UW) {
-      case 1: return launch_uw<B, 1>(a, f32, W, grid, lds, s);
-      case 2: return launch_uw<B, 2>(a, f32, W, grid, lds, s);
-      case 3: case 4: return launch_uw<B, 4>(a, f32, W, grid, lds, s);
-      default: return launch_uw<B, 8>(a, f32, W, grid, lds, s);
-    }
+    if (UW <= 1) return launch_uw<4, 1>(a, grid, threads, lds, s);
+    if (UW <= 2) return launch_uw<4, 2>(a, grid, threads, lds, s);
+    return launch_uw<4, 4>(a, grid, threads, lds, s);
   }
 }
 
@@ -197,15 +270,11 @@ Nf4Split split_levels() {
 extern "C" qw_status qgemv_nf4(const qw_weight *w, const void *x, int B, void *y,
                                qw_dtype y_dtype, void *stream) {
   using namespace qw;
-  if (!w || w->format != QW_FMT_NF4_B64 || !x || !y) return QW_ERR_INVALID_ARG;
-  if (B < 1 || B > 8) return QW_ERR_INVALID_ARG;
-  if (y_dtype != QW_DT_F16 && y_dtype != QW_DT_F32) return QW_ERR_INVALID_ARG;
-  qw_status st = qw_packed_sizes(QW_FMT_NF4_B64, w->N, w->K, w->n_out, nullptr, nullptr,
-                                 nullptr, nullptr);
+  qw_status st = check_weight_view(w, QW_FMT_NF4_B64, 0);
   if (st != QW_OK) return st;
-  if (!w->codes || !w->scales) return QW_ERR_INVALID_ARG;
-  if (!aligned16(w->codes) || !aligned16(w->scales) || !aligned16(x) || !aligned16(y))
-    return QW_ERR_ALIGNMENT;
+  if (!x || !y || B < 1 || B > 8) return QW_ERR_INVALID_ARG;
+  if (y_dtype != QW_DT_F16 && y_dtype != QW_DT_F32) return QW_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y)) return QW_ERR_ALIGNMENT;
   int cus = 0;
   st = current_device(&cus);
   if (st != QW_OK) return st;
@@ -215,19 +284,27 @@ extern "C" qw_status qgemv_nf4(const qw_weight *w, const void *x, int B, void *y
   const int KD = K / 8;
   const int U = (KD + 63) / 64;
   static const Nf4Split sp = split_levels();
+  if ((size_t)w->N * (K / 2) >= (1ull << 31)) return QW_ERR_UNSUPPORTED;
   int b0 = 0;
   while (b0 < B) {
     const int rest = B - b0;
-    const int Bk = rest >= 4 ? 4 : (rest >= 2 ? 2 : 1);
-    const int maxuw = Bk == 1 ? 16 : (Bk == 2 ? 8 : 4);
-    const int W = (U + maxuw - 1) / maxuw;
-    if (W > 8) return QW_ERR_UNSUPPORTED;
-    const int UW = (U + W - 1) / W;
-    int rpw = env_int("QW_GEMV_ROWS_PER_WG", 0);
-    if (rpw <= 0) {
-      const long target_waves = (long)cus * 16;
-      rpw = (int)(((long)w->N * W + target_waves - 1) / target_waves);
-      rpw = max(2, min(rpw, 32));
+    int Bk = rest >= 4 ? 4 : (rest >= 2 ? 2 : 1);
+    auto maxuw = [](int b) { return b == 1 ? 12 : (b == 2 ? 8 : 4); };
+    int W = 0, UW = 0, rpg = 0, grid = 0, threads = 0;
+    size_t lds = 0;
+    for (;;) {
+      W = (U + maxuw(Bk) - 1) / maxuw(Bk);
+      UW = (U + W - 1) / W;
+      const int V = 8 / W;
+      threads = 64 * W * V;
+      const long target_wgs = max(1L, (long)cus * env_int("QW_GEMV_WG_PER_CU", 1));
+      rpg = env_int("QW_GEMV_ROWS_PER_WG", 0);
+      if (rpg <= 0) rpg = (int)max(1L, ((long)w->N + target_wgs - 1) / target_wgs);
+      grid = (w->N + rpg - 1) / rpg;
+      lds = 256 * 8 + (size_t)Bk * K * 2 + (W > 1 ? 4 * (size_t)rpg * W * Bk : 0);
+      if (W <= 8 && lds <= 160 * 1024) break;
+      if (Bk == 1) return QW_ERR_UNSUPPORTED;
+      Bk >>= 1;
     }
     ArgsNf4 a{};
     a.codes = reinterpret_cast<const uint32_t *>(w->codes);
@@ -236,14 +313,14 @@ extern "C" qw_status qgemv_nf4(const qw_weight *w, const void *x, int B, void *y
     a.y = reinterpret_cast<char *>(y) + (size_t)b0 * w->N * esz;
     a.N = w->N;
     a.K = K;
-    a.rows_per_wg = rpw;
+    a.rows_per_wg = rpg;
+    a.W = W;
+    a.f32out = f32 ? 1 : 0;
     a.L = sp;
-    const int grid = (w->N + rpw - 1) / rpw;
-    const size_t lds = 256 * 8 + 4 * (size_t)rpw * W * Bk;
     switch (Bk) {
-      case 1: st = launch_b<1>(a, f32, UW, W, grid, lds, as_stream(stream)); break;
-      case 2: st = launch_b<2>(a, f32, UW, W, grid, lds, as_stream(stream)); break;
-      default: st = launch_b<4>(a, f32, UW, W, grid, lds, as_stream(stream)); break;
+      case 1: st = launch_b<1>(a, UW, grid, threads, lds, as_stream(stream)); break;
+      case 2: st = launch_b<2>(a, UW, grid, threads, lds, as_stream(stream)); break;
+      default: st = launch_b<4>(a, UW, grid, threads, lds, as_stream(stream)); break;
     }
     if (st != QW_OK) return st;
     b0 += Bk;

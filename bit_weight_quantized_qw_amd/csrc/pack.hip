@@ -117,6 +117,25 @@ __global__ __launch_bounds__(256) void anchors_kernel(
   out_w[gid] = v;
 }
 
+// out_mask word i: bit b set iff channel 32*i + b is an anchor channel.
+__global__ __launch_bounds__(256) void mask_kernel(const int32_t *__restrict__ idx, int n_out,
+                                                   int K, uint32_t *__restrict__ mask) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= K / 32) return;
+  const int k0 = 32 * i;
+  int lo = 0, hi = n_out;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (idx[mid] < k0) lo = mid + 1; else hi = mid;
+  }
+  uint32_t m = 0;
+  for (int o = lo; o < n_out && idx[o] < k0 + 32; ++o) {
+    const int b = idx[o] - k0;
+    if (b >= 0) m |= 1u << b;
+  }
+  mask[i] = m;
+}
+
 __global__ __launch_bounds__(256) void pack_nf4_kernel(
     const float *__restrict__ W, int N, int K, Levels16 L,
     uint32_t *__restrict__ codes, float *__restrict__ absmax) {
@@ -240,16 +259,10 @@ extern "C" {
 qw_status qw_pack(const float *W, const qw_weight *dst, void *stream) {
   using namespace qw;
   if (!W || !dst) return QW_ERR_INVALID_ARG;
-  const int N = dst->N, K = dst->K, n_out = dst->n_out;
-  size_t cb, sb, ob;
-  int pad;
-  qw_status st = qw_packed_sizes((qw_format)dst->format, N, K, n_out, &cb, &sb, &ob, &pad);
+  qw_status st = check_weight_view(dst, dst->format, 0);
   if (st != QW_OK) return st;
-  if (!dst->codes || !dst->scales) return QW_ERR_INVALID_ARG;
-  if (n_out > 0 && (!dst->out_idx || !dst->out_w || dst->n_out_pad < pad || dst->n_out_pad % 8))
-    return QW_ERR_INVALID_ARG;
-  if (!aligned16(W) || !aligned16(dst->codes) || !aligned16(dst->scales)) return QW_ERR_ALIGNMENT;
-  if (n_out > 0 && (!aligned16(dst->out_idx) || !aligned16(dst->out_w))) return QW_ERR_ALIGNMENT;
+  if (!aligned16(W)) return QW_ERR_ALIGNMENT;
+  const int N = dst->N, K = dst->K, n_out = dst->n_out;
   st = current_device(nullptr);
   if (st != QW_OK) return st;
   hipStream_t s = as_stream(stream);
@@ -263,6 +276,8 @@ qw_status qw_pack(const float *W, const qw_weight *dst, void *stream) {
       const long cnt = (long)N * dst->n_out_pad;
       anchors_kernel<<<grid_for(cnt, 256), 256, 0, s>>>(W, N, K, dst->out_idx, n_out,
                                                          dst->n_out_pad, dst->out_w);
+      QW_LAUNCH_CHECK();
+      mask_kernel<<<grid_for(K / 32, 256), 256, 0, s>>>(dst->out_idx, n_out, K, dst->out_mask);
       QW_LAUNCH_CHECK();
     }
   } else {

@@ -271,20 +271,11 @@ extern "C" qw_status qgemm_prefill(const qw_weight *w, const void *X, int M, voi
   using namespace qw;
   if (!w || !X || !Y || M < 1) return QW_ERR_INVALID_ARG;
   if (y_dtype != QW_DT_BF16 && y_dtype != QW_DT_F32) return QW_ERR_INVALID_ARG;
-  if (w->format != QW_FMT_2BIT_G32 && w->format != QW_FMT_NF4_B64) return QW_ERR_INVALID_ARG;
-  int pad = 0;
-  qw_status st = qw_packed_sizes((qw_format)w->format, w->N, w->K, w->n_out, nullptr, nullptr,
-                                 nullptr, &pad);
+  if (!w || (w->format != QW_FMT_2BIT_G32 && w->format != QW_FMT_NF4_B64)) return QW_ERR_INVALID_ARG;
+  qw_status st = check_weight_view(w, w->format, 0);
   if (st != QW_OK) return st;
   if (w->K % 64) return QW_ERR_UNSUPPORTED;
-  if (!w->codes || !w->scales) return QW_ERR_INVALID_ARG;
-  if (!aligned16(w->codes) || !aligned16(w->scales) || !aligned16(X) || !aligned16(Y))
-    return QW_ERR_ALIGNMENT;
-  if (w->format == QW_FMT_2BIT_G32 && w->n_out > 0) {
-    if (!w->out_idx || !w->out_w || w->n_out_pad < pad || (w->n_out_pad & 7))
-      return QW_ERR_INVALID_ARG;
-    if (!aligned16(w->out_idx) || !aligned16(w->out_w)) return QW_ERR_ALIGNMENT;
-  }
+  if (!aligned16(X) || !aligned16(Y)) return QW_ERR_ALIGNMENT;
   st = current_device(nullptr);
   if (st != QW_OK) return st;
   PrefillArgs a{};

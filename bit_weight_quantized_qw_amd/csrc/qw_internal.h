@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/qw.h"
+#include "qw.h"
 
 namespace qw {
 
@@ -36,6 +36,10 @@ const float *nf4_levels_host();
 
 // Returns the padded anchor row stride for n_out anchors.
 inline int pad8(int n) { return (n + 7) & ~7; }
+
+// Validates a packed-weight view against its format (sizes, NULLs,
+// alignment of every buffer it uses). K_expect > 0 also pins K.
+qw_status check_weight_view(const qw_weight *w, int format, int K_expect);
 
 // ---------------------------------------------------------------------------
 // Exact fp64 -> fp16 round-to-nearest-even, subnormals kept, by integer

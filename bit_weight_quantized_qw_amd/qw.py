@@ -42,6 +42,14 @@ class qw_weight(ctypes.Structure):
         ("n_out", ctypes.c_int32), ("n_out_pad", ctypes.c_int32),
         ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
         ("out_idx", ctypes.c_void_p), ("out_w", ctypes.c_void_p),
+        ("out_mask", ctypes.c_void_p),
+    ]
+
+
+class qw_sizes(ctypes.Structure):
+    _fields_ = [
+        ("codes", ctypes.c_size_t), ("scales", ctypes.c_size_t), ("out_idx", ctypes.c_size_t),
+        ("out_w", ctypes.c_size_t), ("out_mask", ctypes.c_size_t), ("n_out_pad", ctypes.c_int32),
     ]
 
 
@@ -62,8 +70,7 @@ def lib():
     sig = {
         "qw_abi_version": (c_i, []),
         "qw_status_str": (ctypes.c_char_p, [c_i]),
-        "qw_packed_sizes": (c_i, [c_i, c_i, c_i, c_i, ctypes.POINTER(c_sz), ctypes.POINTER(c_sz),
-                                  ctypes.POINTER(c_sz), ctypes.POINTER(c_i)]),
+        "qw_packed_sizes": (c_i, [c_i, c_i, c_i, c_i, ctypes.POINTER(qw_sizes)]),
         "qw_outlier_count": (c_i, [c_i, c_d]),
         "qw_codebook_2bit": (c_i, [ctypes.POINTER(ctypes.c_float)]),
         "qw_nf4_levels": (c_i, [ctypes.POINTER(ctypes.c_float)]),
@@ -107,11 +114,11 @@ def qw_status_str(status):
 
 
 def qw_packed_sizes(fmt, N, K, n_out=0):
-    cb, sb, ob = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
-    pad = ctypes.c_int()
-    _check(lib().qw_packed_sizes(fmt, N, K, n_out, ctypes.byref(cb), ctypes.byref(sb),
-                                 ctypes.byref(ob), ctypes.byref(pad)), "qw_packed_sizes")
-    return cb.value, sb.value, ob.value, pad.value
+    """Dict of buffer byte counts and the anchor row stride."""
+    z = qw_sizes()
+    _check(lib().qw_packed_sizes(fmt, N, K, n_out, ctypes.byref(z)), "qw_packed_sizes")
+    return {"codes": z.codes, "scales": z.scales, "out_idx": z.out_idx, "out_w": z.out_w,
+            "out_mask": z.out_mask, "n_out_pad": z.n_out_pad}
 
 
 def qw_outlier_count(K, frac):
@@ -137,23 +144,26 @@ class PackedWeight:
 
     def __init__(self, fmt, N, K, n_out=0, device="cuda"):
         import torch
-        cb, sb, ob, pad = qw_packed_sizes(fmt, N, K, n_out)
-        self.format, self.N, self.K, self.n_out, self.n_out_pad = fmt, N, K, n_out, pad
-        self.codes = torch.empty(cb, dtype=torch.uint8, device=device)
-        self.scales = torch.empty(sb, dtype=torch.uint8, device=device)
-        self.out_idx = torch.empty(max(n_out, 1), dtype=torch.int32, device=device) if n_out else None
-        self.out_w = torch.empty(max(ob // 2, 1), dtype=torch.int16, device=device) if n_out else None
+        z = qw_packed_sizes(fmt, N, K, n_out)
+        self.format, self.N, self.K, self.n_out, self.n_out_pad = fmt, N, K, n_out, z["n_out_pad"]
+        self.codes = torch.empty(z["codes"], dtype=torch.uint8, device=device)
+        self.scales = torch.empty(z["scales"], dtype=torch.uint8, device=device)
+        self.out_idx = self.out_w = self.out_mask = None
+        if n_out:
+            self.out_idx = torch.empty(n_out, dtype=torch.int32, device=device)
+            self.out_w = torch.empty(z["out_w"] // 2, dtype=torch.int16, device=device)
+            self.out_mask = torch.empty(z["out_mask"] // 4, dtype=torch.int32, device=device)
 
     def view(self):
+        p = lambda t: t.data_ptr() if t is not None else None
         return qw_weight(self.format, self.N, self.K, self.n_out, self.n_out_pad,
                          self.codes.data_ptr(), self.scales.data_ptr(),
-                         self.out_idx.data_ptr() if self.out_idx is not None else None,
-                         self.out_w.data_ptr() if self.out_w is not None else None)
+                         p(self.out_idx), p(self.out_w), p(self.out_mask))
 
     def nbytes(self):
         n = self.codes.numel() + self.scales.numel()
         if self.n_out:
-            n += self.out_idx.numel() * 4 + self.out_w.numel() * 2
+            n += self.out_idx.numel() * 4 + self.out_w.numel() * 2 + self.out_mask.numel() * 4
         return n
 
     # host copies in the oracle's array shapes

@@ -27,7 +27,9 @@
  *                both IEEE fp16 bit patterns.
  *  anchors       out_idx int32 [n_out], strictly ascending, in [0, K);
  *                out_w fp16 [N][n_out_pad], n_out_pad = n_out rounded up to a
- *                multiple of 8, padding zero.
+ *                multiple of 8, padding zero;
+ *                out_mask uint32 [K/32], bit (k % 32) of word k / 32 set iff
+ *                channel k is an anchor (derived from out_idx by qw_pack).
  *  NF4 codes     uint8 [N][K/2]; low nibble = element 2j, high = 2j+1.
  *  NF4 scales    float [N][K/64] (absmax per block of 64 along K).
  *
@@ -36,8 +38,7 @@
  *    current HIP device; "host" pointers to host memory. The caller owns
  *    and frees all memory; nothing is retained after the call returns.
  *  - ``stream`` is a hipStream_t passed as void* (NULL = default stream).
- *    Device work is only enqueued; no entry point synchronizes, except
- *    qw_select_outliers (see there).
+ *    Device work is only enqueued; no entry point synchronizes.
  *  - arguments are validated on the host before anything is enqueued; on
  *    any error nothing is enqueued and the status says why. A failed launch
  *    returns QW_ERR_HIP. No entry point aborts or throws.
@@ -86,7 +87,14 @@ typedef struct {
   void *scales;       /* 2-bit: uint16 [N][K/32][2]; NF4: float [N][K/64] */
   int32_t *out_idx;   /* [n_out] or NULL when n_out == 0 */
   uint16_t *out_w;    /* fp16 [N][n_out_pad] or NULL when n_out == 0 */
+  uint32_t *out_mask; /* [K/32] or NULL when n_out == 0 */
 } qw_weight;
+
+/* Byte counts of the buffers of one packed matrix (0 when unused). */
+typedef struct {
+  size_t codes, scales, out_idx, out_w, out_mask;
+  int32_t n_out_pad;
+} qw_sizes;
 
 /* Version of this ABI (QW_ABI_VERSION). */
 int qw_abi_version(void);
@@ -94,14 +102,12 @@ int qw_abi_version(void);
 /* Static text for a status code. Never NULL. */
 const char *qw_status_str(qw_status s);
 
-/* Bytes the caller must allocate for a packed matrix of the given format
- * and shape, and the anchor row stride. Host only; any output pointer may
- * be NULL. Errors: QW_ERR_INVALID_ARG if N, K <= 0, K not a multiple of the
- * group/block size (32 for 2-bit, 64 for NF4), n_out < 0, n_out >= K, or
- * n_out > 0 for NF4. */
-qw_status qw_packed_sizes(qw_format fmt, int N, int K, int n_out,
-                          size_t *codes_bytes, size_t *scales_bytes,
-                          size_t *out_w_bytes, int *n_out_pad);
+/* Bytes the caller must allocate for each buffer of a packed matrix of the
+ * given format and shape, and the anchor row stride, into host struct *out.
+ * Host only. Errors: QW_ERR_INVALID_ARG if out is NULL, N, K <= 0, K not a
+ * multiple of the group/block size (32 for 2-bit, 64 for NF4), n_out < 0,
+ * n_out >= K, or n_out > 0 for NF4. */
+qw_status qw_packed_sizes(qw_format fmt, int N, int K, int n_out, qw_sizes *out);
 
 /* Number of anchor channels for a fraction of K: floor(frac * K) in double
  * precision (section 4 keeps the top 3.5%). Returns -1 if K < 0 or frac is
@@ -139,7 +145,7 @@ qw_status qw_select_outliers(const float *W, int N, int K, const float *X_prof,
  *   W        device fp32 [N][K]
  *   dst->out_idx (2-bit, n_out > 0) device int32 [n_out], strictly ascending;
  *            those columns are zeroed before the fit and copied to out_w
- *            rounded to fp16 (nearest-even).
+ *            rounded to fp16 (nearest-even); out_mask is written from it.
  * 2-bit: per group of 32 along K, in fp64 without fused multiply-add:
  * mean m and population variance v; code q = (w-m >= 0 ? 2 : 1) moved to
  * the outer level (3 or 0) when (w-m)^2 > t^2 v with t = (C[2]+C[3])/2;

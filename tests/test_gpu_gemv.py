@@ -56,7 +56,7 @@ def test_gemv_2bit_14b_shape_with_anchors(B):
 
 
 @pytest.mark.parametrize("N,K,n_anchor", [(1, 32, 0), (7, 96, 2), (33, 1056, 5), (130, 2080, 0),
-                                          (64, 3072, 40), (5, 27648, 967)])
+                                          (64, 3072, 40), (5, 27648, 967), (300, 27648, 967)])
 @pytest.mark.parametrize("B", [1, 2, 4])
 def test_gemv_2bit_ragged(N, K, n_anchor, B):
     W = inputs.weight(N, K, workload=70)

@@ -66,21 +66,25 @@ def test_outlier_count_rejects_bad_fraction(L):
 
 
 def test_packed_sizes(L):
-    assert qw.qw_packed_sizes(qw.QW_FMT_2BIT_G32, 13824, 5120, 179) == (
-        13824 * 1280, 13824 * 160 * 4, 13824 * 184 * 2, 184)
-    assert qw.qw_packed_sizes(qw.QW_FMT_NF4_B64, 11008, 4096, 0) == (
-        11008 * 2048, 11008 * 64 * 4, 0, 0)
+    z = qw.qw_packed_sizes(qw.QW_FMT_2BIT_G32, 13824, 5120, 179)
+    assert z == {"codes": 13824 * 1280, "scales": 13824 * 160 * 4, "out_idx": 179 * 4,
+                 "out_w": 13824 * 184 * 2, "out_mask": 160 * 4, "n_out_pad": 184}
+    z = qw.qw_packed_sizes(qw.QW_FMT_NF4_B64, 11008, 4096, 0)
+    assert z == {"codes": 11008 * 2048, "scales": 11008 * 64 * 4, "out_idx": 0,
+                 "out_w": 0, "out_mask": 0, "n_out_pad": 0}
     for bad in [(qw.QW_FMT_2BIT_G32, 0, 64, 0), (qw.QW_FMT_2BIT_G32, 4, 48, 0),
                 (qw.QW_FMT_NF4_B64, 4, 96, 0), (qw.QW_FMT_NF4_B64, 4, 128, 3),
                 (qw.QW_FMT_2BIT_G32, 4, 64, 64), (7, 4, 64, 0)]:
         with pytest.raises(qw.QwError) as e:
             qw.qw_packed_sizes(*bad)
         assert e.value.status == qw.QW_ERR_INVALID_ARG
+    assert L.qw_packed_sizes(qw.QW_FMT_2BIT_G32, 4, 64, 0, None) == qw.QW_ERR_INVALID_ARG
 
 
 def _view(fmt, N, K, n_out=0, ptr=0x1000):
     pad = (n_out + 7) // 8 * 8 if n_out else 0
-    return qw.qw_weight(fmt, N, K, n_out, pad, ptr, ptr, ptr if n_out else None, ptr if n_out else None)
+    return qw.qw_weight(fmt, N, K, n_out, pad, ptr, ptr, ptr if n_out else None,
+                        ptr if n_out else None, ptr if n_out else None)
 
 
 def test_validation_before_device_work(L):
@@ -101,7 +105,7 @@ def test_validation_before_device_work(L):
     vb = _view(qw.QW_FMT_2BIT_G32, 16, 64, ptr=0x1008)
     assert L.qw_pack(p, ctypes.byref(vb), s) == qw.QW_ERR_ALIGNMENT
     # anchors declared without buffers
-    va = qw.qw_weight(qw.QW_FMT_2BIT_G32, 16, 64, 3, 8, 0x1000, 0x1000, None, None)
+    va = qw.qw_weight(qw.QW_FMT_2BIT_G32, 16, 64, 3, 8, 0x1000, 0x1000, None, None, None)
     assert L.qgemv_2bit(ctypes.byref(va), p, 1, p, qw.QW_DT_F16, s) == qw.QW_ERR_INVALID_ARG
     # prefill needs K % 64
     v96 = _view(qw.QW_FMT_2BIT_G32, 16, 96)
