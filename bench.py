@@ -17,13 +17,15 @@ synthetic input for the chosen workload:
   copy_calib              -- a plain device copy of 1 GiB (counter scale).
 
 Timing: after W untimed steps, the stream is pre-loaded with a GPU sleep,
-then exactly K steps are enqueued with a HIP event between consecutive
-kernels, so the device runs them back to back; synchronize on both sides.
-value = algorithmic bytes (GEMV) or flops (GEMM) of K steps / time of the
-K steps between the first and last event. Each GEMV weight set is rotated
-over copies totalling >= 1 GiB so HBM, not the 256 MB last-level cache,
-serves it. roofline.achieved uses the dominant kernel's own average
-duration from the same events. cpu_baseline times the fp64 oracle on the
+then exactly K steps are enqueued back to back between two HIP events;
+synchronize on both sides. value = algorithmic bytes (GEMV) or flops
+(GEMM) of K steps / time between those two events. Each GEMV weight set
+is rotated over copies totalling >= 1 GiB so HBM, not the 256 MB
+last-level cache, serves it. Every launch in the timed region also carries
+a pair of HIP events that the library attaches to its own kernel dispatch
+(qw_time_next_call), so the pair brackets the kernel's execution alone;
+roofline.achieved = the dominant kernel's algorithmic amount per launch /
+its average duration from those pairs (the figure a kernel trace reports). cpu_baseline times the fp64 oracle on the
 host (product path from packed arrays) on a bounded sample.
 """
 
@@ -54,6 +56,7 @@ def log(*a):
 class Workload:
     """launches(i): list of (kernel_name, callable) making up step i."""
     name = ""
+    library = True  # every launch is one libqw entry-point call
     unit = "GB/s"
     bound = "hbm"
     dtype = "f16"
@@ -383,6 +386,7 @@ class Prefill70b(Workload):
 
 class CopyCalib(Workload):
     name = "copy_calib"
+    library = False  # a torch kernel: timed with events recorded around it
 
     def __init__(self):
         import torch
@@ -425,6 +429,20 @@ def _time_oracle(fn, amount, sample, budget_s=12.0, scale=1e9):
             "sample": f"{n} x {sample}", "seconds": round(dt, 2)}
 
 
+def _traffic(path, workload, kernel):
+    """Counter-derived HBM bytes per launch, or None when there is no entry
+    or the kernel's sources changed since the counters were taken."""
+    import hashlib
+    try:
+        e = json.load(open(path))[workload][kernel]
+        h = hashlib.sha256()
+        for f in e["sources"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        return e["bytes"] if h.hexdigest() == e["sha256"] else None
+    except (OSError, KeyError, ValueError, TypeError):
+        return None
+
+
 WORKLOADS = {
     "llama7b_mlp_up_gemv": Llama7bMlpUp,
     "single_layer_2048": SingleLayer2048,
@@ -451,45 +469,63 @@ def _sleep_rate():
 
 
 def run(wl, steps, warmup):
+    """Returns (ms of the K timed steps, {kernel: [ms per launch]}, wall ms)."""
+    import ctypes
     import torch
+    from bit_weight_quantized_qw_amd import qw
+    L = qw.lib()
     for i in range(warmup):
         for _, f in wl.launches(i):
             f()
     torch.cuda.synchronize()
-    # measure host enqueue cost to size the pre-load sleep
+    # per-launch kernel events (the library attaches them to its own
+    # dispatches, so each pair brackets the kernel's execution only)
+    plan = [wl.launches(warmup + i) for i in range(steps)]
+    pairs = []
+    for step in plan:
+        for name, _ in step:
+            s_ev = torch.cuda.Event(enable_timing=True)
+            e_ev = torch.cuda.Event(enable_timing=True)
+            pairs.append((name, s_ev, e_ev, qw._event_handle(s_ev), qw._event_handle(e_ev)))
+    torch.cuda.synchronize()
+    # host enqueue cost, to size the sleep that keeps the device queue full
     t0 = time.perf_counter()
-    evs = []
     for i in range(warmup):
         for _, f in wl.launches(i):
-            ev = torch.cuda.Event(enable_timing=True)
-            ev.record()
+            if wl.library:
+                L.qw_time_next_call(pairs[0][3], pairs[0][4])
             f()
     torch.cuda.synchronize()
     per_step = (time.perf_counter() - t0) / max(warmup, 1)
     rate = _sleep_rate()
     sleep_ms = min(30000.0, 1.5 * per_step * steps * 1e3 + 5.0)
 
-    names, events = [], []
+    first = torch.cuda.Event(enable_timing=True)
+    last = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     torch.cuda._sleep(int(rate * sleep_ms))
-    first = torch.cuda.Event(enable_timing=True)
     first.record()
-    events.append(first)
-    for i in range(steps):
-        for name, f in wl.launches(warmup + i):
-            f()
-            ev = torch.cuda.Event(enable_timing=True)
-            ev.record()
-            names.append(name)
-            events.append(ev)
+    j = 0
+    for step in plan:
+        for _, f in step:
+            _, s_ev, e_ev, hs, he = pairs[j]
+            if wl.library:
+                L.qw_time_next_call(hs, he)
+                f()
+            else:
+                s_ev.record()
+                f()
+                e_ev.record()
+            j += 1
+    last.record()
     torch.cuda.synchronize()
     t_wall1 = time.perf_counter()
-    total_ms = events[0].elapsed_time(events[-1])
+    total_ms = first.elapsed_time(last)
     per_kernel = {}
-    for j, nm in enumerate(names):
-        per_kernel.setdefault(nm, []).append(events[j].elapsed_time(events[j + 1]))
-    return total_ms, per_kernel, (t_wall1 - t_wall0) * 1e3, sleep_ms
+    for name, s_ev, e_ev, _, _ in pairs:
+        per_kernel.setdefault(name, []).append(s_ev.elapsed_time(e_ev))
+    return total_ms, per_kernel, (t_wall1 - t_wall0) * 1e3
 
 
 def main():
@@ -516,7 +552,7 @@ def main():
     wl = WORKLOADS[args.workload]()
     log(f"workload {wl.name}: setup done")
     torch.cuda.synchronize()
-    total_ms, per_kernel, wall_ms, sleep_ms = run(wl, args.steps, args.warmup)
+    total_ms, per_kernel, wall_ms = run(wl, args.steps, args.warmup)
     ms_per_step = total_ms / args.steps
     scale = 1e12 if wl.unit == "TFLOP/s" else 1e9
     value = wl.step_amount() / (ms_per_step * 1e-3) / scale
@@ -530,12 +566,7 @@ def main():
     dominant = max(kstats, key=lambda k: kstats[k]["avg_us"] * kstats[k]["launches"])
     peak = BF16_PEAK_TFLOPS if wl.bound == "mfma" else HBM_PEAK_GBS
     ach = kstats[dominant]["achieved"]
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        try:
-            traffic = json.load(open(args.traffic_json)).get(wl.name, {}).get(dominant)
-        except Exception:
-            traffic = None
+    traffic = _traffic(args.traffic_json, wl.name, dominant)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": wl.unit, "n_gpus": 1,

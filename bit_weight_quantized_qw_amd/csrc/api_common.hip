@@ -5,6 +5,8 @@
 
 #include <mutex>
 
+#include <hip/hip_ext.h>
+
 #include "qw_internal.h"
 
 #pragma STDC FP_CONTRACT OFF
@@ -108,9 +110,38 @@ qw_status check_weight_view(const qw_weight *w, int format, int K_expect) {
   return QW_OK;
 }
 
+// Events armed by qw_time_next_call on this host thread, and the pair taken
+// by the entry point currently running on it.
+namespace {
+thread_local hipEvent_t tl_armed_start = nullptr, tl_armed_stop = nullptr;
+thread_local hipEvent_t tl_call_start = nullptr, tl_call_stop = nullptr;
+}  // namespace
+
+CallScope::CallScope() {
+  tl_call_start = tl_armed_start;
+  tl_call_stop = tl_armed_stop;
+  tl_armed_start = tl_armed_stop = nullptr;
+}
+
+CallScope::~CallScope() { tl_call_start = tl_call_stop = nullptr; }
+
+hipError_t launch_raw(const void *fn, dim3 grid, dim3 block, void **argv, size_t lds,
+                      hipStream_t s) {
+  if (!tl_call_start && !tl_call_stop) return hipLaunchKernel(fn, grid, block, argv, lds, s);
+  hipEvent_t start = tl_call_start;
+  tl_call_start = nullptr;  // only the call's first kernel records the start
+  return hipExtLaunchKernel(fn, grid, block, argv, lds, s, start, tl_call_stop, 0);
+}
+
 }  // namespace qw
 
 extern "C" {
+
+qw_status qw_time_next_call(void *start_event, void *stop_event) {
+  qw::tl_armed_start = reinterpret_cast<hipEvent_t>(start_event);
+  qw::tl_armed_stop = reinterpret_cast<hipEvent_t>(stop_event);
+  return QW_OK;
+}
 
 int qw_abi_version(void) { return QW_ABI_VERSION; }
 

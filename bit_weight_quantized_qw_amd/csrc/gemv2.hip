@@ -144,12 +144,14 @@ extern "C" {
 
 qw_status qgemv_2bit(const qw_weight *w, const void *x, int B, void *y, qw_dtype y_dtype,
                      void *stream) {
+  qw::CallScope scope;
   void *ys[1] = {y};
   return qw::gemv2::launch(w, 1, x, B, ys, y_dtype, qw::as_stream(stream));
 }
 
 qw_status qgemv_2bit_grouped(const qw_weight *ws, int count, const void *x, int B,
                              void *const *ys, qw_dtype y_dtype, void *stream) {
+  qw::CallScope scope;
   return qw::gemv2::launch(ws, count, x, B, ys, y_dtype, qw::as_stream(stream));
 }
 

@@ -458,8 +458,7 @@ qw_status launch_one(const Args &a, int grid, int threads, size_t lds, hipStream
     QW_HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(&kernel<B, UW, UA>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
   }
-  kernel<B, UW, UA><<<grid, threads, lds, s>>>(a);
-  QW_LAUNCH_CHECK();
+  QW_HIP_TRY(launch(kernel<B, UW, UA>, grid, threads, lds, s, a));
   return QW_OK;
 }
 

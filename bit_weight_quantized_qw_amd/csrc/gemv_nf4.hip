@@ -65,11 +65,18 @@ __device__ inline uint32_t bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32
 }
 
 constexpr uint32_t kOob = 0x7FFFFFF0u;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// Upper bound on the 16-byte x loads one thread issues while staging x
+// (the host checks ceil(B*K/8 / threads) against it).
+constexpr int kXLoads = 16;
 
 // LDS: table uint2 [256] | x uint32 [B][K/2] | parts float [rows_per_wg][W][B]
 template <int B, int UW>
 __global__ __launch_bounds__(512) void gemv_nf4_kernel(ArgsNf4 a) {
-  constexpr int RU0 = (B == 1 ? 48 : 24) / (2 * UW);
+  // Both row buffers (2 loads per row and code dword) stay within the 63
+  // loads one wave can have outstanding, so the wait that precedes the x
+  // staging covers only the x loads.
+  constexpr int RU0 = 60 / (2 * 2 * UW);
   constexpr int RU = RU0 < 1 ? 1 : (RU0 > 8 ? 8 : RU0);
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   uint2 *table = reinterpret_cast<uint2 *>(lds);
@@ -100,37 +107,70 @@ __global__ __launch_bounds__(512) void gemv_nf4_kernel(ArgsNf4 a) {
     vm[j] = u < KD ? (uint32_t)(u >> 3) * 4 : kOob;
   }
   uint32_t cA[RU][UW], cB[RU][UW], mA[RU][UW], mB[RU][UW];
+  // Rows past the worker's range read through a zero-length descriptor, so
+  // every load is unconditional (no branch for the wait counters to merge).
+  const auto rz = make_rsrc(a.codes, 0u);
   auto load = [&](uint32_t (&c)[RU][UW], uint32_t (&m)[RU][UW], int rb) {
 #pragma unroll
     for (int i = 0; i < RU; ++i) {
       const int rr = rb + i;
-      if (rr < r1) {
-        const uint32_t so_c = (uint32_t)rr * KD * 4, so_m = (uint32_t)rr * KB * 4;
+      const bool ok = rr < r1;
+      const auto rcr = ok ? rc : rz, rmr = ok ? rm : rz;
+      const uint32_t so_c = ok ? (uint32_t)rr * KD * 4 : 0u, so_m = ok ? (uint32_t)rr * KB * 4 : 0u;
 #pragma unroll
-        for (int j = 0; j < UW; ++j) {
-          c[i][j] = bload(rc, vc[j], so_c);
-          m[i][j] = bload(rm, vm[j], so_m);
-        }
+      for (int j = 0; j < UW; ++j) {
+        c[i][j] = bload(rcr, vc[j], so_c);
+        m[i][j] = bload(rmr, vm[j], so_m);
       }
     }
   };
+
+  // This group's copy of x: 16-byte buffer loads issued ahead of the weight
+  // prefetch, so the LDS stores below wait only for them.
+  const auto rx = make_rsrc(a.x, (uint32_t)((size_t)B * K * 2));
+  const int nx = (B * KD + T - 1) / T;  // uniform trip count
+  constexpr int XMAX = kXLoads;
+  u32x4 xv[XMAX];
+#pragma unroll
+  for (int q = 0; q < XMAX; ++q) {
+    if (q < nx) {
+      const int i = q * T + (int)threadIdx.x;
+      xv[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, i < B * KD ? i * 16 : (int)kOob, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
   load(cA, mA, r0);
   load(cB, mB, r0 + RU);
+  __builtin_amdgcn_sched_barrier(0);
 
-  // level-pair table and this group's copy of x
+  // level-pair table
+  // (levels picked by a select chain over scalar kernel arguments: a
+  // per-lane indexed read of the argument block would be a memory load
+  // queued behind the weight prefetch)
   for (int v = threadIdx.x; v < 256; v += T) {
     const int q0 = v & 15, q1 = v >> 4;
+    uint32_t h0 = a.L.hi[0], l0 = a.L.lo[0], h1 = a.L.hi[0], l1 = a.L.lo[0];
+#pragma unroll
+    for (int t = 1; t < 16; ++t) {
+      h0 = q0 == t ? a.L.hi[t] : h0;
+      l0 = q0 == t ? a.L.lo[t] : l0;
+      h1 = q1 == t ? a.L.hi[t] : h1;
+      l1 = q1 == t ? a.L.lo[t] : l1;
+    }
     uint2 e;
-    e.x = (uint32_t)a.L.hi[q0] | ((uint32_t)a.L.hi[q1] << 16);
-    e.y = (uint32_t)a.L.lo[q0] | ((uint32_t)a.L.lo[q1] << 16);
+    e.x = h0 | (h1 << 16);
+    e.y = l0 | (l1 << 16);
     table[v] = e;
   }
-  for (int i = threadIdx.x; i < B * KD; i += T) {
-    const int b = i / KD, u = i - b * KD;
-    reinterpret_cast<uint4 *>(xl)[i] =
-        *reinterpret_cast<const uint4 *>(a.x + (size_t)b * K + (size_t)u * 8);
+#pragma unroll
+  for (int q = 0; q < XMAX; ++q) {
+    const int i = q * T + (int)threadIdx.x;
+    if (q < nx && i < B * KD) reinterpret_cast<u32x4 *>(xl)[i] = xv[q];
   }
-  __syncthreads();
+  // LDS-only barrier: a full __syncthreads would also drain the prefetch.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
   uint32_t xr[UW][B][4];
 #pragma unroll
@@ -138,9 +178,9 @@ __global__ __launch_bounds__(512) void gemv_nf4_kernel(ArgsNf4 a) {
     const int u = (j * W + w) * 64 + lane;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (u < KD) v = reinterpret_cast<const uint4 *>(xl)[b * KD + u];
-      xr[j][b][0] = v.x; xr[j][b][1] = v.y; xr[j][b][2] = v.z; xr[j][b][3] = v.w;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (u < KD) v = reinterpret_cast<const u32x4 *>(xl)[b * KD + u];
+      xr[j][b][0] = v[0]; xr[j][b][1] = v[1]; xr[j][b][2] = v[2]; xr[j][b][3] = v[3];
     }
   }
 
@@ -219,8 +259,7 @@ qw_status launch_uw(const ArgsNf4 &a, int grid, int threads, size_t lds, hipStre
     QW_HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_nf4_kernel<B, UW>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
   }
-  gemv_nf4_kernel<B, UW><<<grid, threads, lds, s>>>(a);
-  QW_LAUNCH_CHECK();
+  QW_HIP_TRY(launch(gemv_nf4_kernel<B, UW>, grid, threads, lds, s, a));
   return QW_OK;
 }
 
@@ -270,6 +309,7 @@ Nf4Split split_levels() {
 extern "C" qw_status qgemv_nf4(const qw_weight *w, const void *x, int B, void *y,
                                qw_dtype y_dtype, void *stream) {
   using namespace qw;
+  CallScope scope;
   qw_status st = check_weight_view(w, QW_FMT_NF4_B64, 0);
   if (st != QW_OK) return st;
   if (!x || !y || B < 1 || B > 8) return QW_ERR_INVALID_ARG;
@@ -302,7 +342,7 @@ extern "C" qw_status qgemv_nf4(const qw_weight *w, const void *x, int B, void *y
       if (rpg <= 0) rpg = (int)max(1L, ((long)w->N + target_wgs - 1) / target_wgs);
       grid = (w->N + rpg - 1) / rpg;
       lds = 256 * 8 + (size_t)Bk * K * 2 + (W > 1 ? 4 * (size_t)rpg * W * Bk : 0);
-      if (W <= 8 && lds <= 160 * 1024) break;
+      if (W <= 8 && lds <= 160 * 1024 && (Bk * KD + threads - 1) / threads <= kXLoads) break;
       if (Bk == 1) return QW_ERR_UNSUPPORTED;
       Bk >>= 1;
     }

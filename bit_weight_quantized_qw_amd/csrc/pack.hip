@@ -258,6 +258,7 @@ extern "C" {
 
 qw_status qw_pack(const float *W, const qw_weight *dst, void *stream) {
   using namespace qw;
+  CallScope scope;
   if (!W || !dst) return QW_ERR_INVALID_ARG;
   qw_status st = check_weight_view(dst, dst->format, 0);
   if (st != QW_OK) return st;
@@ -268,27 +269,26 @@ qw_status qw_pack(const float *W, const qw_weight *dst, void *stream) {
   hipStream_t s = as_stream(stream);
   if (dst->format == QW_FMT_2BIT_G32) {
     const long groups = (long)N * (K / 32);
-    pack2_kernel<<<grid_for(groups, 256), 256, 0, s>>>(
-        W, N, K, dst->out_idx, n_out, reinterpret_cast<uint32_t *>(dst->codes),
-        reinterpret_cast<uint32_t *>(dst->scales));
-    QW_LAUNCH_CHECK();
+    QW_HIP_TRY(launch(pack2_kernel, grid_for(groups, 256), 256, 0, s, W, N, K,
+                      (const int32_t *)dst->out_idx, n_out,
+                      reinterpret_cast<uint32_t *>(dst->codes),
+                      reinterpret_cast<uint32_t *>(dst->scales)));
     if (n_out > 0) {
       const long cnt = (long)N * dst->n_out_pad;
-      anchors_kernel<<<grid_for(cnt, 256), 256, 0, s>>>(W, N, K, dst->out_idx, n_out,
-                                                         dst->n_out_pad, dst->out_w);
-      QW_LAUNCH_CHECK();
-      mask_kernel<<<grid_for(K / 32, 256), 256, 0, s>>>(dst->out_idx, n_out, K, dst->out_mask);
-      QW_LAUNCH_CHECK();
+      QW_HIP_TRY(launch(anchors_kernel, grid_for(cnt, 256), 256, 0, s, W, N, K,
+                        (const int32_t *)dst->out_idx, n_out, (int)dst->n_out_pad,
+                        dst->out_w));
+      QW_HIP_TRY(launch(mask_kernel, grid_for(K / 32, 256), 256, 0, s,
+                        (const int32_t *)dst->out_idx, n_out, K, dst->out_mask));
     }
   } else {
     Levels16 L;
     const float *h = nf4_levels_host();
     for (int i = 0; i < 16; ++i) L.v[i] = h[i];
     const long blocks = (long)N * (K / 64);
-    pack_nf4_kernel<<<grid_for(blocks, 256), 256, 0, s>>>(
-        W, N, K, L, reinterpret_cast<uint32_t *>(dst->codes),
-        reinterpret_cast<float *>(dst->scales));
-    QW_LAUNCH_CHECK();
+    QW_HIP_TRY(launch(pack_nf4_kernel, grid_for(blocks, 256), 256, 0, s, W, N, K, L,
+                      reinterpret_cast<uint32_t *>(dst->codes),
+                      reinterpret_cast<float *>(dst->scales)));
   }
   return QW_OK;
 }
@@ -296,6 +296,7 @@ qw_status qw_pack(const float *W, const qw_weight *dst, void *stream) {
 qw_status qw_select_outliers(const float *W, int N, int K, const float *X_prof, int P,
                              double frac, qw_score score, int32_t *out_idx, void *stream) {
   using namespace qw;
+  CallScope scope;
   if (!W || !X_prof || N <= 0 || K <= 0 || P <= 0) return QW_ERR_INVALID_ARG;
   if (score != QW_SCORE_MEANABS && score != QW_SCORE_L2) return QW_ERR_INVALID_ARG;
   const int n = qw_outlier_count(K, frac);
@@ -311,16 +312,12 @@ qw_status qw_select_outliers(const float *W, int N, int K, const float *X_prof, 
   QW_HIP_TRY(hipMallocAsync(&scratch, bytes, s));
   double *sc = reinterpret_cast<double *>(scratch);
   int32_t *flag = reinterpret_cast<int32_t *>(sc + K);
-  score_kernel<<<grid_for(K, 256), 256, 0, s>>>(W, N, K, X_prof, P, (int)score, sc);
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess) {
-    rank_kernel<<<grid_for(K, 256), 256, 0, s>>>(sc, K, n, flag);
-    e = hipGetLastError();
-  }
-  if (e == hipSuccess) {
-    compact_kernel<<<1, 1024, 0, s>>>(flag, K, n, out_idx);
-    e = hipGetLastError();
-  }
+  hipError_t e = launch(score_kernel, grid_for(K, 256), 256, 0, s, W, N, K, X_prof, P,
+                        (int)score, sc);
+  if (e == hipSuccess)
+    e = launch(rank_kernel, grid_for(K, 256), 256, 0, s, (const double *)sc, K, n, flag);
+  if (e == hipSuccess)
+    e = launch(compact_kernel, 1, 1024, 0, s, (const int32_t *)flag, K, n, out_idx);
   hipError_t fe = hipFreeAsync(scratch, s);
   if (e != hipSuccess || fe != hipSuccess) return QW_ERR_HIP;
   return QW_OK;

@@ -256,10 +256,9 @@ qw_status launch_fmt(const PrefillArgs &a, bool f32, hipStream_t s) {
   const int grid = a.mt_count * nt;
   const size_t lds = (size_t)(BM + BN) * LDA * 2 + (FMT == QW_FMT_NF4_B64 ? 256 * 8 : 0);
   if (f32)
-    prefill_kernel<FMT, true><<<grid, NT, lds, s>>>(a);
+    QW_HIP_TRY(launch(prefill_kernel<FMT, true>, grid, NT, lds, s, a));
   else
-    prefill_kernel<FMT, false><<<grid, NT, lds, s>>>(a);
-  QW_LAUNCH_CHECK();
+    QW_HIP_TRY(launch(prefill_kernel<FMT, false>, grid, NT, lds, s, a));
   return QW_OK;
 }
 
@@ -269,6 +268,7 @@ qw_status launch_fmt(const PrefillArgs &a, bool f32, hipStream_t s) {
 extern "C" qw_status qgemm_prefill(const qw_weight *w, const void *X, int M, void *Y,
                                    qw_dtype y_dtype, void *stream) {
   using namespace qw;
+  CallScope scope;
   if (!w || !X || !Y || M < 1) return QW_ERR_INVALID_ARG;
   if (y_dtype != QW_DT_BF16 && y_dtype != QW_DT_F32) return QW_ERR_INVALID_ARG;
   if (!w || (w->format != QW_FMT_2BIT_G32 && w->format != QW_FMT_NF4_B64)) return QW_ERR_INVALID_ARG;

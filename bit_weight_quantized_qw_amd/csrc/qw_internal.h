@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 #include "qw.h"
 
 namespace qw {
@@ -15,12 +18,35 @@ namespace qw {
     if (qw_e_ != hipSuccess) return QW_ERR_HIP;            \
   } while (0)
 
-// After a <<<>>> launch: picks up launch-configuration errors.
-#define QW_LAUNCH_CHECK()                                  \
-  do {                                                     \
-    hipError_t qw_e_ = hipGetLastError();                  \
-    if (qw_e_ != hipSuccess) return QW_ERR_HIP;            \
-  } while (0)
+// ---------------------------------------------------------------------------
+// Kernel launches and per-call timing (qw_time_next_call). Every entry point
+// that enqueues kernels opens a CallScope before validating its arguments;
+// launch() attaches the armed events of that scope to the kernels it
+// dispatches (start on the first, stop on every one).
+struct CallScope {
+  CallScope();
+  ~CallScope();
+  CallScope(const CallScope &) = delete;
+  CallScope &operator=(const CallScope &) = delete;
+};
+
+hipError_t launch_raw(const void *fn, dim3 grid, dim3 block, void **argv, size_t lds,
+                      hipStream_t s);
+
+template <typename Tup, size_t... I>
+inline void fill_argv(Tup &t, void **argv, std::index_sequence<I...>) {
+  ((argv[I] = (void *)&std::get<I>(t)), ...);
+}
+
+template <typename... P, typename... A>
+inline hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                         A &&...args) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  std::tuple<P...> t(std::forward<A>(args)...);
+  void *argv[sizeof...(P) + 1];
+  fill_argv(t, argv, std::index_sequence_for<P...>{});
+  return launch_raw(reinterpret_cast<const void *>(kernel), grid, block, argv, lds, s);
+}
 
 inline bool aligned16(const void *p) {
   return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;

@@ -24,7 +24,7 @@ QW_SCORE_MEANABS, QW_SCORE_L2 = 1, 2
 
 # every function declared in include/qw.h
 EXPORTS = [
-    "qw_abi_version", "qw_status_str", "qw_packed_sizes", "qw_outlier_count",
+    "qw_abi_version", "qw_status_str", "qw_time_next_call", "qw_packed_sizes", "qw_outlier_count",
     "qw_codebook_2bit", "qw_nf4_levels", "qw_select_outliers", "qw_pack",
     "qgemv_2bit", "qgemv_nf4", "qgemv_2bit_grouped", "qgemm_prefill",
 ]
@@ -70,6 +70,7 @@ def lib():
     sig = {
         "qw_abi_version": (c_i, []),
         "qw_status_str": (ctypes.c_char_p, [c_i]),
+        "qw_time_next_call": (c_i, [c_p, c_p]),
         "qw_packed_sizes": (c_i, [c_i, c_i, c_i, c_i, ctypes.POINTER(qw_sizes)]),
         "qw_outlier_count": (c_i, [c_i, c_d]),
         "qw_codebook_2bit": (c_i, [ctypes.POINTER(ctypes.c_float)]),
@@ -111,6 +112,21 @@ def qw_abi_version():
 
 def qw_status_str(status):
     return lib().qw_status_str(int(status)).decode()
+
+
+def _event_handle(ev):
+    if ev is None:
+        return ctypes.c_void_p(0)
+    if not ev.cuda_event:  # torch creates the HIP event at its first record
+        ev.record()
+    return ctypes.c_void_p(ev.cuda_event)
+
+
+def qw_time_next_call(start_event, stop_event):
+    """Arm the next library call on this thread to record kernel start/stop
+    into two torch.cuda.Event(enable_timing=True) objects (either may be None)."""
+    _check(lib().qw_time_next_call(_event_handle(start_event), _event_handle(stop_event)),
+           "qw_time_next_call")
 
 
 def qw_packed_sizes(fmt, N, K, n_out=0):

@@ -102,6 +102,19 @@ int qw_abi_version(void);
 /* Static text for a status code. Never NULL. */
 const char *qw_status_str(qw_status s);
 
+/* Kernel timing without launch gaps, for benchmarks and profilers. Arms the
+ * next call of qw_select_outliers, qw_pack, qgemv_2bit, qgemv_nf4,
+ * qgemv_2bit_grouped or qgemm_prefill made on the calling host thread: the
+ * first kernel that call dispatches records start_event when it begins
+ * executing, and each of its kernels records stop_event when it ends, so
+ * after the call the pair brackets exactly the device execution of its
+ * kernels (hipExtLaunchKernel semantics). Both are hipEvent_t passed as
+ * void*, created by the caller on the current device; either may be NULL.
+ * The pair is consumed by that next call even when it returns an error
+ * before launching anything (then neither event is recorded).
+ * qw_time_next_call(NULL, NULL) disarms. Host only; returns QW_OK. */
+qw_status qw_time_next_call(void *start_event, void *stop_event);
+
 /* Bytes the caller must allocate for each buffer of a packed matrix of the
  * given format and shape, and the anchor row stride, into host struct *out.
  * Host only. Errors: QW_ERR_INVALID_ARG if out is NULL, N, K <= 0, K not a

@@ -157,3 +157,23 @@ def test_gemv_nf4_fp16_out_is_rounded_fp32_out():
     x = inputs.act_f16(2, 1024, workload=76)
     np.testing.assert_array_equal(_run_nf4(W, x).astype(np.float16),
                                   _run_nf4(W, x, f32=True).astype(np.float16))
+
+
+def test_timed_call_records_kernel_duration_and_same_result():
+    import torch
+    W = inputs.weight(4096, 4096, workload=77)
+    x = f16_dev(inputs.act_f16(1, 4096, workload=77))
+    pw = _packed_2bit(W)
+    y0 = qw.qgemv_2bit(pw, x, out_dtype=torch.float32)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    qw.qw_time_next_call(s, e)
+    y1 = qw.qgemv_2bit(pw, x, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e)
+    print(f"timed qgemv_2bit 4096x4096: {ms * 1e3:.2f} us")
+    assert 0.0 < ms < 50.0
+    assert torch.equal(y0, y1)
+    # the pair was consumed: a second call does not re-record it
+    qw.qgemv_2bit(pw, x, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert s.elapsed_time(e) == ms

@@ -124,3 +124,11 @@ def test_valid_call_without_gpu_reports_no_device(L):
     v = _view(qw.QW_FMT_2BIT_G32, 16, 64)
     p = ctypes.c_void_p(0x1000)
     assert L.qgemv_2bit(ctypes.byref(v), p, 1, p, qw.QW_DT_F16, s) == qw.QW_ERR_NO_DEVICE
+
+
+def test_time_next_call_is_host_only_and_disarms(L):
+    assert L.qw_time_next_call(None, None) == qw.QW_OK
+    # an armed pair is consumed by the next call even when it fails validation
+    assert L.qw_time_next_call(ctypes.c_void_p(0x10), ctypes.c_void_p(0x20)) == qw.QW_OK
+    assert L.qgemv_2bit(None, None, 1, None, qw.QW_DT_F16, None) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_time_next_call(None, None) == qw.QW_OK
