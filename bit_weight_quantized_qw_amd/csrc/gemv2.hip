@@ -5,6 +5,11 @@
 #include "gemv2_kernel.h"
 
 namespace qw {
+namespace gemv2m {
+qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void *const *ys,
+                 bool f32, int cus, hipStream_t s);
+}  // namespace gemv2m
+
 namespace gemv2 {
 namespace {
 
@@ -113,8 +118,22 @@ qw_status launch(const qw_weight *ws, int count, const void *x, int B, void *con
     // buffer offsets are 32-bit
     if ((size_t)ws[i].N * (ws[i].K / 4) >= (1ull << 31)) return QW_ERR_UNSUPPORTED;
   }
-  // batch rows go through kernels of width 4, 2 and 1 (e.g. 7 = 4 + 2 + 1),
+  // the matrix-core kernel takes the whole batch in one pass when the shape
+  // fits it; otherwise batch rows go through vector-ALU kernels of width 4,
+  // 2 and 1 (e.g. 7 = 4 + 2 + 1),
   // narrower when the x slice of a wider one does not fit
+  // Path choice (measured on MI355X): the matrix-core kernel for batches of
+  // two or more; at batch 1 only for large matrices with K <= 8192, where it
+  // is at least as fast. QW_GEMV_VALU=1 forces the vector-ALU kernel and
+  // QW_GEMV_VALU=0 the matrix-core one where it applies (for tests).
+  long nk = 0;
+  for (int i = 0; i < count; ++i) nk += (long)ws[i].N * ws[i].K;
+  const int force = env_int("QW_GEMV_VALU", -1);
+  const bool mc = force == 0 || (force < 0 && (B >= 2 || (K <= 8192 && nk >= (16L << 20))));
+  if (mc) {
+    st = gemv2m::launch(ws, count, reinterpret_cast<const uint16_t *>(x), B, ys, f32, cus, s);
+    if (st != QW_ERR_UNSUPPORTED) return st;
+  }
   int b0 = 0;
   while (b0 < B) {
     const int rest = B - b0;

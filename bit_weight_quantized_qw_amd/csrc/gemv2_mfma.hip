@@ -1,0 +1,692 @@
+// Decode GEMV against the adaptive non-uniform 2-bit code on the matrix
+// cores ("On-The-Fly Weight Synthesizer (OTF-LLM Engine v4.0)": codebook of
+// section 2, per-group scale/offset of section 3, fp16 anchors of section 4).
+//
+//   y[b][n] = sum_g S_g * (C0 X_g + d1 sum_{k in g} x_R q + d3 sum_{k in g} x_R h)
+//           + Z_g X_g + sum_o x[b][idx_o] W_O[n][o]
+//
+// with q = l + 2h the code, d1 = C1 - C0, d3 = (C2 - C0) - 2 d1 (exact for
+// the symmetric codebook: C3 - C0 = d1 + (C2 - C0)) and X_g the group sum of
+// x_R (x with the anchor channels zeroed).
+//
+// The two code sums run on v_mfma_scale_f32_16x16x128_f8f6f4 with the codes
+// as the fp4 (e2m1) operand and x as the fp8 (e4m3) operand:
+//  * a 2-bit code masked into the low two bits of a nibble is the e2m1 value
+//    q/2 exactly, its high bit alone (bit 1) is the e2m1 value h; one AND
+//    (plus one shift per 16 codes) turns 8 packed codes into 8 operands;
+//  * x is split exactly into three e4m3 limbs after scaling each group of 32
+//    by a power of two 2^s (max |x| 2^s in [128, 256)); a limb only loses
+//    what underflows e4m3 (below 2^-10 absolute, 2^-17 of the group max);
+//  * the matrix core sums each run of 8 products aligned to the largest of
+//    them, dropping bits below 2^-13 of it; every D row holds one limb, so a
+//    run never mixes limbs and only elements below about 2^-8 of their run's
+//    largest lose bits.
+// Operand placement (one 16x16x128 instruction = 16 output rows x 4 groups):
+//  * B (codes, fp4): lane l holds output row l%16 and the 32 codes of one
+//    group ("slot" l/16), as nibbles in the order even codes 0..14, odd
+//    1..15, even 16..30, odd 17..31;
+//  * A (x limbs, fp8): row i = 4*slot + limb (limb 3 zero); the 16 bytes of a
+//    lane hold limb values of half a group in the same permuted order, in
+//    bytes 0..15 for slots 0, 1 and bytes 16..31 for slots 2, 3;
+//  * D: lane l holds rows 4*(l/16)..+3 of column l%16, i.e. the three limb
+//    partials of (output row l%16, slot l/16) -- the same (row, group) whose
+//    codes and S, Z that lane loaded, so the group's scale is applied in the
+//    lane that owns it.
+// Work: a wave computes 16 output rows; its K range is cut in super-chunks of
+// 512 (16 groups, 4 instructions per stream), streamed through a ring of P
+// register slots (two 16-byte code loads and two 8-byte S/Z loads per lane),
+// followed by anchor chunks of 96 anchors per row on the same ring.
+// A workgroup of 8 waves owns a contiguous range of 16-row tiles; each tile's
+// K range may be split over several waves, whose partial row sums meet in LDS
+// and are added in a fixed order.
+#include <stdlib.h>
+
+#include "qw_internal.h"
+
+namespace qw {
+namespace gemv2m {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMats = 4;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kXItems = 12;  // 16-byte x loads per thread in the prologue
+constexpr int kIdxItems = 4; // anchor indices per thread in the prologue
+constexpr int kAnchorChunk = 96;
+#ifndef QW_GEMV_EARLY_SLOTS
+#define QW_GEMV_EARLY_SLOTS 2
+#endif
+// ring slots requested before the x preparation (the rest after it): more
+// start the weight stream earlier but delay the preparation behind them
+constexpr int kEarly = QW_GEMV_EARLY_SLOTS;
+constexpr uint32_t kOob = 0x7FFFFFF0u;
+
+struct Mat {
+  const uint32_t *codes;  // [N][K/16]
+  const uint32_t *sz;     // [N][K/32]: fp16 S | fp16 Z << 16
+  const uint32_t *mask;   // [K/32] anchor-channel bits, null without anchors
+  const int32_t *idx;     // [n_out]
+  const uint16_t *wo;     // [N][n_out_pad] fp16
+  void *y;                // [B][N]
+  int N, n_out, n_out_pad;
+  int wg_begin, wg_count;  // this matrix's workgroups
+  int tiles;               // ceil(N / 16)
+  int W;                   // waves per tile (K splits); divides K/512
+};
+
+struct Args {
+  Mat m[kMats];
+  int count;
+  const uint16_t *x;  // [B][K] fp16
+  int K;
+  int f32out;
+  int xo_len;         // anchor index slots in LDS (multiple of 96)
+  int units_max;      // max tiles per workgroup * W (partials in LDS)
+};
+
+// LDS layout, bytes:
+//   limbs  [B][G][3][32]   e4m3 limbs per group (two 16-byte halves)
+//   zero   [32]
+//   coef   [B][G] float4   {2 d1 2^-s, d3 2^-s, C0 X_g, X_g}
+//   aidx   [xo_len] int32  anchor channels (entries past n_out unused)
+//   xo     [B][xo_len] fp16 x at the anchor channels, zero past n_out
+//   xraw   [B][K + 8] fp16 x as given, 8 zeros after each row (read at K)
+//   parts  [units_max][16][B] float  partial row sums of the units
+struct Lds {
+  size_t limbs, zero, coef, aidx, xo, xraw, parts, total;
+};
+
+__host__ __device__ inline Lds lds_layout(int B, int K, int xo_len, int units_max) {
+  const size_t G = (size_t)K / 32;
+  Lds l;
+  l.limbs = 0;
+  l.zero = (size_t)B * G * 96;
+  l.coef = l.zero + 32;
+  l.aidx = l.coef + (size_t)B * G * 16;
+  l.xo = l.aidx + (((size_t)xo_len * 4 + 15) & ~(size_t)15);
+  l.xraw = l.xo + (((size_t)B * xo_len * 2 + 15) & ~(size_t)15);
+  l.parts = l.xraw + (size_t)B * (K + 8) * 2;
+  l.total = l.parts + (size_t)units_max * 16 * B * 4;
+  return l;
+}
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ inline uint32_t ld1(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)v, (int)s, 0);
+}
+__device__ inline u32x2 ld2(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, (int)v, (int)s, 0);
+}
+__device__ inline u32x4 ld4(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)v, (int)s, 0);
+}
+
+__device__ inline v4f mfma_x_codes(v8i a_fp8, v8i b_fp4) {
+  const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+  // A format 0 = e4m3, B format 4 = e2m1; scales 0x7f = 2^0
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_fp8, b_fp4, z, 0, 4, 0, 0x7f, 0, 0x7f);
+}
+
+__device__ inline float h2f(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+__device__ inline float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), c, false);
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ inline float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                CTRL, ROW_MASK, 0xF, false));
+}
+
+// e4m3 bytes of four floats: a0, a1 in bytes 0, 1 and b0, b1 in bytes 2, 3
+__device__ inline uint32_t to_fp8x4(float a0, float a1, float b0, float b1) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(b0, b1, lo, true);
+}
+__device__ inline float fp8_at(uint32_t w, int byte) {
+  switch (byte) {
+    case 0: return __builtin_amdgcn_cvt_f32_fp8((int)w, 0);
+    case 1: return __builtin_amdgcn_cvt_f32_fp8((int)w, 1);
+    case 2: return __builtin_amdgcn_cvt_f32_fp8((int)w, 2);
+    default: return __builtin_amdgcn_cvt_f32_fp8((int)w, 3);
+  }
+}
+
+// Position of one wave in its stream of steps: unit (tile, split) and the
+// step inside it (code super-chunks first, then anchor chunks). Units of a
+// wave are u = wave, wave + 8, ...; unit u is (tile u / W, split u % W) and
+// split s owns anchor chunks s, s + W, ... below NA. Kept incrementally so
+// that advancing needs no division except once per unit.
+struct Cursor {
+  int unit;   // local unit index; >= n_units means past the end
+  int tile;   // local tile index (unit / W)
+  int split;  // unit % W
+  int step;   // step inside the unit
+  int len;    // steps of this unit
+};
+
+struct Stream {
+  int n_units, W, L, NA;
+  __device__ int unit_len(int split) const {
+    return L + (split < NA ? (NA - 1 - split) / W + 1 : 0);
+  }
+  __device__ Cursor start(int u) const {
+    Cursor c;
+    c.unit = u;
+    c.tile = u / W;
+    c.split = u - c.tile * W;
+    c.step = 0;
+    c.len = unit_len(c.split);
+    return c;
+  }
+  __device__ void advance(Cursor &c) const {
+    if (++c.step >= c.len) {
+      c.unit += kWaves;
+      c.split += kWaves;
+      while (c.split >= W) {
+        c.split -= W;
+        ++c.tile;
+      }
+      c.step = 0;
+      c.len = unit_len(c.split);
+    }
+  }
+};
+
+// Select among four values that are all read (so the reads are not
+// conditional: no chain of dependent scalar loads behind branches).
+template <typename T>
+__device__ inline T sel4(int i, T v0, T v1, T v2, T v3) {
+  T r = v0;
+  r = i == 1 ? v1 : r;
+  r = i == 2 ? v2 : r;
+  r = i == 3 ? v3 : r;
+  return r;
+}
+
+template <int B, int P, bool MULTI>
+__global__ __launch_bounds__(kThreads) void kernel(Args a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  int mi = 0;
+  if (MULTI) {
+#pragma unroll
+    for (int i = 1; i < kMats; ++i)
+      if (i < a.count && (int)blockIdx.x >= a.m[i].wg_begin) mi = i;
+  }
+  // each field picked with constant indices (scalar selects, no copy of the
+  // argument block into private memory)
+#define QW_SEL(f) (MULTI ? sel4(mi, a.m[0].f, a.m[1].f, a.m[2].f, a.m[3].f) : a.m[0].f)
+  struct {
+    const uint32_t *codes, *sz, *mask;
+    const int32_t *idx;
+    const uint16_t *wo;
+    void *y;
+    int N, n_out, n_out_pad, wg_begin, wg_count, tiles, W;
+  } M = {QW_SEL(codes), QW_SEL(sz),    QW_SEL(mask),      QW_SEL(idx),      QW_SEL(wo),
+         QW_SEL(y),     QW_SEL(N),     QW_SEL(n_out),     QW_SEL(n_out_pad), QW_SEL(wg_begin),
+         QW_SEL(wg_count), QW_SEL(tiles), QW_SEL(W)};
+#undef QW_SEL
+  const int K = a.K;
+  const int G = K >> 5;
+  const int SC = K >> 9;
+  const int wi = (int)blockIdx.x - M.wg_begin;
+  // (wi + 1) * tiles < 2^31: tiles <= 2^27 and workgroups per matrix <= 16
+  // per CU of a 256-CU part are checked on the host
+  const int t0 = (int)((uint32_t)(wi * M.tiles) / (uint32_t)M.wg_count);
+  const int t1 = (int)((uint32_t)((wi + 1) * M.tiles) / (uint32_t)M.wg_count);
+  const int W = M.W;
+  const int L = SC / W;
+  const int NA = (M.n_out_pad + kAnchorChunk - 1) / kAnchorChunk;
+  const int n_units = (t1 - t0) * W;
+  const Lds lay = lds_layout(B, K, a.xo_len, a.units_max);
+  uint8_t *limbs = lds + lay.limbs;
+  uint8_t *zero = lds + lay.zero;
+  float4 *coef = reinterpret_cast<float4 *>(lds + lay.coef);
+  int32_t *aidx_l = reinterpret_cast<int32_t *>(lds + lay.aidx);
+  uint16_t *xo = reinterpret_cast<uint16_t *>(lds + lay.xo);
+  uint16_t *xraw = reinterpret_cast<uint16_t *>(lds + lay.xraw);
+  float *parts = reinterpret_cast<float *>(lds + lay.parts);
+  const int KX = K + 8;  // xraw row stride
+
+  const int j = lane & 15;  // output row in the tile; A row
+  const int g = lane >> 4;  // slot (group) of this lane's codes and D
+  // ---- stream bookkeeping (wave-uniform) ----
+  Stream st{n_units, W, L, NA};
+
+  // ---- per-lane load offsets ----
+  const uint32_t rb_c = (uint32_t)K / 4;           // code bytes per row
+  const uint32_t rb_s = (uint32_t)K / 8;           // S/Z bytes per row
+  const uint32_t rb_a = (uint32_t)M.n_out_pad * 2; // anchor bytes per row
+  const uint32_t n_codes = (uint32_t)((size_t)M.N * rb_c);
+  const uint32_t n_sz = (uint32_t)((size_t)M.N * rb_s);
+  const uint32_t n_wo = (uint32_t)((size_t)M.N * rb_a);
+
+  // ring slot = three 16-byte loads per lane. Code step: lane (row j,
+  // slot g) takes groups 16 sc + 4g .. +3 of its row: codes bytes [32g, 32g+32)
+  // of the super-chunk's 128 and their four S/Z words. Anchor step: three
+  // pieces of 8 anchor weights. One branch-free issue path: descriptor and
+  // offsets are picked per step kind.
+  struct Slot {
+    u32x4 c0, c1, c2;
+  };
+  Slot ring[P];
+  auto issue = [&](Slot &dst, const Cursor &c) __attribute__((always_inline)) {
+    const bool live = c.unit < n_units;
+    const int tile = t0 + (live ? c.tile : 0);
+    const int split = live ? c.split : 0;
+    const bool row_ok = live && tile * 16 + j < M.N;
+    const bool code = c.step < L;
+    const int sc = split * L + c.step;
+    const int an = split + W * (c.step - L);
+    // descriptors built from a selected base and size (size 0 past the end)
+    const auto r01 = rsrc(code ? (const void *)M.codes : (const void *)M.wo,
+                          !live ? 0u : (code ? n_codes : n_wo));
+    const auto r2 = rsrc(code ? (const void *)M.sz : (const void *)M.wo,
+                         !live ? 0u : (code ? n_sz : n_wo));
+    const uint32_t s01 = !live ? 0u : (code ? (uint32_t)tile * 16 * rb_c + (uint32_t)sc * 128
+                                            : (uint32_t)tile * 16 * rb_a);
+    const uint32_t s2 = !live ? 0u : (code ? (uint32_t)tile * 16 * rb_s + (uint32_t)sc * 64
+                                           : (uint32_t)tile * 16 * rb_a);
+    const uint32_t pa = (uint32_t)an * (kAnchorChunk * 2) + 16u * g;  // anchor piece 0
+    uint32_t v0, v1, v2;
+    if (code) {  // uniform
+      v0 = row_ok ? (uint32_t)j * rb_c + 32u * g : kOob;
+      v1 = row_ok ? v0 + 16 : kOob;
+      v2 = row_ok ? (uint32_t)j * rb_s + 16u * g : kOob;
+    } else {
+      v0 = row_ok && pa < rb_a ? (uint32_t)j * rb_a + pa : kOob;
+      v1 = row_ok && pa + 64 < rb_a ? (uint32_t)j * rb_a + pa + 64 : kOob;
+      v2 = row_ok && pa + 128 < rb_a ? (uint32_t)j * rb_a + pa + 128 : kOob;
+    }
+    dst.c0 = ld4(r01, v0, s01);
+    dst.c1 = ld4(r01, v1, s01);
+    dst.c2 = ld4(r2, v2, s2);
+  };
+
+  // ---- prologue loads: x (16 bytes per item), anchor mask, anchor indices ----
+  const int n_items = B * G * 4;  // (b, group, quarter)
+  const auto r_x = rsrc(a.x, (uint32_t)((size_t)B * K * 2));
+  const auto r_mask = rsrc(M.mask, M.mask ? (uint32_t)G * 4 : 0u);
+  const auto r_idx = rsrc(M.idx, (uint32_t)M.n_out * 4);
+  u32x4 xv[kXItems];
+  uint32_t mk[kXItems];
+  const bool has_mask = M.mask != nullptr;
+#pragma unroll
+  for (int q = 0; q < kXItems; ++q) {
+    xv[q] = u32x4{0, 0, 0, 0};
+    mk[q] = 0;
+    if (q * kThreads < n_items) {  // uniform; these are the wave's first loads
+      const int it = q * kThreads + (int)threadIdx.x;
+      const bool ok = it < n_items;
+      const int bg = it >> 2, qt = it & 3;
+      int b = 0;
+#pragma unroll
+      for (int t = 1; t < B; ++t) b += bg >= t * G;
+      const int gr = bg - b * G;
+      xv[q] = ld4(r_x, ok ? (uint32_t)((b * K + gr * 32 + qt * 8) * 2) : kOob, 0);
+      if (has_mask) mk[q] = ld1(r_mask, ok ? (uint32_t)gr * 4 : kOob, 0);
+    }
+  }
+  uint32_t aidx[kIdxItems];  // valid where q * kThreads + tid < n_out
+#pragma unroll
+  for (int q = 0; q < kIdxItems; ++q) {
+    aidx[q] = 0;
+    if (q * kThreads < M.n_out) {  // uniform
+      const int o = q * kThreads + (int)threadIdx.x;
+      aidx[q] = ld1(r_idx, o < M.n_out ? (uint32_t)o * 4 : kOob, 0);
+    }
+  }
+  // ---- weight prefetch: the first P steps (every ring load is
+  //      unconditional, so the waits below count exactly) ----
+  Cursor cl = st.start(wave);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < kEarly; ++i) {
+    issue(ring[i], cl);
+    st.advance(cl);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- x preparation: limbs, coefficients, raw copy ----
+  {
+    const float C0 = -1.52f, C1 = -0.45f, C2 = 0.45f;
+    const float d1 = C1 - C0, d3 = (C2 - C0) - 2.0f * d1;
+#pragma unroll
+    for (int q = 0; q < kXItems; ++q) {
+      if (q * kThreads < n_items) {  // uniform: whole quads stay together
+        const int it = q * kThreads + (int)threadIdx.x;
+        const bool ok = it < n_items;
+        const int bg = it >> 2, qt = it & 3;
+        int b = 0;
+#pragma unroll
+      for (int t = 1; t < B; ++t) b += bg >= t * G;
+      const int gr = bg - b * G;
+        const uint32_t om = (mk[q] >> (qt * 8)) & 0xFFu;
+        uint32_t d[4] = {xv[q][0], xv[q][1], xv[q][2], xv[q][3]};
+        if (ok) {
+          uint32_t *raw = reinterpret_cast<uint32_t *>(xraw + (size_t)b * KX + gr * 32 + qt * 8);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) raw[i] = d[i];
+        }
+        float xf[8];
+        float amax = 0.0f, xs = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t h = (d[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+          xf[i] = ((om >> i) & 1u) ? 0.0f : h2f(h);
+          amax = fmaxf(amax, fabsf(xf[i]));
+          xs += xf[i];
+        }
+        // the four quarters of a group are lanes 4m..4m+3
+        amax = fmaxf(amax, dpp_f<0xB1, 0xF>(amax));
+        amax = fmaxf(amax, dpp_f<0x4E, 0xF>(amax));
+        xs += dpp_f<0xB1, 0xF>(xs);
+        xs += dpp_f<0x4E, 0xF>(xs);
+        const int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) : 8;
+        const int sh = 8 - e;  // amax * 2^sh in [128, 256)
+        float r[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[i] = __builtin_ldexpf(xf[i], sh);
+        // element 8qt+i sits in half qt/2 at byte (i even) 4(qt&1)+i/2 or
+        // (i odd) 8+4(qt&1)+i/2
+        uint8_t *hb = limbs + ((size_t)(b * G + gr) * 3) * 32 + (qt >> 1) * 16 + 4 * (qt & 1);
+#pragma unroll
+        for (int lb = 0; lb < 3; ++lb) {
+          const uint32_t ev = to_fp8x4(r[0], r[2], r[4], r[6]);
+          const uint32_t od = to_fp8x4(r[1], r[3], r[5], r[7]);
+          if (ok) {
+            *reinterpret_cast<uint32_t *>(hb + lb * 32) = ev;
+            *reinterpret_cast<uint32_t *>(hb + lb * 32 + 8) = od;
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            r[2 * i] -= fp8_at(ev, i);
+            r[2 * i + 1] -= fp8_at(od, i);
+          }
+        }
+        if (ok && qt == 0) {
+          const float inv = __builtin_ldexpf(1.0f, -sh);
+          coef[b * G + gr] = make_float4(2.0f * d1 * inv, d3 * inv, C0 * xs, xs);
+        }
+      }
+    }
+    if (threadIdx.x < 8) reinterpret_cast<uint32_t *>(zero)[threadIdx.x] = 0u;
+    if (threadIdx.x < 8 * B) xraw[(threadIdx.x >> 3) * KX + K + (threadIdx.x & 7)] = 0;
+#pragma unroll
+    for (int q = 0; q < kIdxItems; ++q) {
+      const int o = q * kThreads + (int)threadIdx.x;
+      if (q * kThreads < a.xo_len && o < a.xo_len) aidx_l[o] = (int)aidx[q];
+    }
+  }
+  // LDS-only barrier: the weight prefetch stays in flight
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+#pragma unroll
+  for (int i = kEarly; i < P; ++i) {
+    issue(ring[i], cl);
+    st.advance(cl);
+  }
+
+  // anchor x gathered once (zero past n_out; indices clamped to the zeros
+  // at K), then a second LDS-only barrier
+  for (int o = threadIdx.x; o < a.xo_len; o += kThreads) {
+    const uint32_t ci = o < M.n_out ? min((uint32_t)aidx_l[o], (uint32_t)K) : (uint32_t)K;
+#pragma unroll
+    for (int b = 0; b < B; ++b) xo[b * a.xo_len + o] = xraw[(size_t)b * KX + ci];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+
+  // ---- per-lane A-operand addresses ----
+  const int s_a = j >> 2, limb = j & 3;
+  const bool a_ok = limb < 3 && ((g >> 1) == (s_a & 1));
+  const int a_lane = (4 * s_a) * 96 + limb * 32 + (g & 1) * 16;  // plus 96 * chunk group
+  const bool a_hi = (s_a >> 1) != 0;
+
+  float acc[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+
+  auto finish_unit = [&](int u) __attribute__((always_inline)) {
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      float v = acc[b];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (lane < 16) parts[((size_t)u * 16 + j) * B + b] = v;
+      acc[b] = 0.0f;
+    }
+  };
+
+  auto compute = [&](const Slot &src, const Cursor &c) __attribute__((always_inline)) {
+    const int split = c.split;
+    if (c.step < L) {
+      const int sc = split * L + c.step;
+      // chunk ch covers groups 16 sc + ch + 4 s of slots s = 0..3; this
+      // lane's codes and S/Z are those of slot g
+      v8i bq[4], bh[4];
+      float S[4], Z[4];
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) {
+        const u32x4 &cw = (ch >> 1) ? src.c1 : src.c0;
+        const uint32_t c0 = cw[(ch & 1) * 2], c1 = cw[(ch & 1) * 2 + 1];
+        const uint32_t c0s = c0 >> 2, c1s = c1 >> 2;
+        bq[ch] = v8i{(int)(c0 & 0x33333333u), (int)(c0s & 0x33333333u),
+                     (int)(c1 & 0x33333333u), (int)(c1s & 0x33333333u), 0, 0, 0, 0};
+        bh[ch] = v8i{(int)(c0 & 0x22222222u), (int)(c0s & 0x22222222u),
+                     (int)(c1 & 0x22222222u), (int)(c1s & 0x22222222u), 0, 0, 0, 0};
+        const uint32_t szw = src.c2[ch];
+        S[ch] = h2f(szw & 0xFFFFu);
+        Z[ch] = h2f(szw >> 16);
+      }
+#pragma unroll
+      for (int b = 0; b < B; ++b) {
+        // all operand and coefficient reads first, then the eight products,
+        // then the epilogues: LDS and matrix-core latencies overlap
+        const int gb = b * G + 16 * sc;
+        const uint8_t *pa = limbs + (size_t)gb * 96 + a_lane;
+        const uint8_t *p_lo = a_ok && !a_hi ? pa : zero;
+        const uint8_t *p_hi = a_ok && a_hi ? pa : zero;
+        const int st_lo = a_ok && !a_hi ? 96 : 0, st_hi = a_ok && a_hi ? 96 : 0;
+        u32x4 lo[4], hi[4];
+        float4 cf[4];
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) {
+          lo[ch] = *reinterpret_cast<const u32x4 *>(p_lo + ch * st_lo);
+          hi[ch] = *reinterpret_cast<const u32x4 *>(p_hi + ch * st_hi);
+        }
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) cf[ch] = coef[gb + ch + 4 * g];
+        v4f dq[4], dh[4];
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) {
+          const v8i A = {(int)lo[ch][0], (int)lo[ch][1], (int)lo[ch][2], (int)lo[ch][3],
+                         (int)hi[ch][0], (int)hi[ch][1], (int)hi[ch][2], (int)hi[ch][3]};
+          dq[ch] = mfma_x_codes(A, bq[ch]);
+          dh[ch] = mfma_x_codes(A, bh[ch]);
+        }
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) {
+          const float pq = (dq[ch][0] + dq[ch][1]) + dq[ch][2];
+          const float ph = (dh[ch][0] + dh[ch][1]) + dh[ch][2];
+          const float t = __builtin_fmaf(pq, cf[ch].x, __builtin_fmaf(ph, cf[ch].y, cf[ch].z));
+          acc[b] = __builtin_fmaf(S[ch], t, acc[b]);
+          acc[b] = __builtin_fmaf(Z[ch], cf[ch].w, acc[b]);
+        }
+      }
+    } else {
+      const int an = split + W * (c.step - L);
+      const u32x4 pc[3] = {src.c0, src.c1, src.c2};
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int o = an * kAnchorChunk + 8 * (g + 4 * i);
+        // o + 8 <= xo_len always (xo_len is a multiple of 96)
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const u32x4 xv4 = *reinterpret_cast<const u32x4 *>(xo + b * a.xo_len + o);
+#pragma unroll
+          for (int p = 0; p < 4; ++p) acc[b] = dot2(xv4[p], pc[i][p], acc[b]);
+        }
+      }
+    }
+  };
+
+  Cursor cc = st.start(wave);
+  while (cc.unit < n_units) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      // consumers are conditional, the refill is not (past the end it reads
+      // through a zero-size descriptor), so every slot's loads stay in order
+      const bool on = cc.unit < n_units;  // uniform
+      const int u = cc.unit;
+      const bool last = on && cc.step + 1 >= cc.len;
+      if (on) compute(ring[i], cc);
+      issue(ring[i], cl);
+      st.advance(cl);
+      if (on) st.advance(cc);
+      if (last) finish_unit(u);
+    }
+  }
+
+  // ---- partial row sums of every unit -> y, splits added in order ----
+  __syncthreads();
+  const int rows = (t1 - t0) * 16;
+  for (int t = threadIdx.x; t < rows * B; t += kThreads) {
+    const int rl = t / B, b = t - rl * B;
+    const int tl = rl >> 4, jj = rl & 15;
+    const int row = t0 * 16 + rl;
+    if (row >= M.N) continue;
+    float v = 0.0f;
+    for (int sp = 0; sp < W; ++sp) v += parts[((size_t)(tl * W + sp) * 16 + jj) * B + b];
+    const size_t off = (size_t)b * M.N + row;
+    if (a.f32out)
+      reinterpret_cast<float *>(M.y)[off] = v;
+    else
+      reinterpret_cast<_Float16 *>(M.y)[off] = (_Float16)v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+
+namespace {
+
+template <int B, int P, bool MULTI>
+qw_status launch_bpm(const Args &a, int grid, size_t lds, hipStream_t s) {
+  if (lds > 64 * 1024) {
+    QW_HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(&kernel<B, P, MULTI>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+  }
+  QW_HIP_TRY(launch(kernel<B, P, MULTI>, grid, kThreads, lds, s, a));
+  return QW_OK;
+}
+
+template <int B, int P>
+qw_status launch_bp(const Args &a, int grid, size_t lds, hipStream_t s) {
+  return a.count > 1 ? launch_bpm<B, P, true>(a, grid, lds, s) : launch_bpm<B, P, false>(a, grid, lds, s);
+}
+
+qw_status launch_b(const Args &a, int B, int grid, size_t lds, hipStream_t s) {
+  switch (B) {
+    case 1: return launch_bp<1, 6>(a, grid, lds, s);
+    case 2: return launch_bp<2, 6>(a, grid, lds, s);
+    case 3: return launch_bp<3, 4>(a, grid, lds, s);
+    case 4: return launch_bp<4, 4>(a, grid, lds, s);
+    case 5: return launch_bp<5, 4>(a, grid, lds, s);
+    case 6: return launch_bp<6, 4>(a, grid, lds, s);
+    case 7: return launch_bp<7, 4>(a, grid, lds, s);
+    default: return launch_bp<8, 4>(a, grid, lds, s);
+  }
+}
+
+// Waves per tile: a divisor of the super-chunk count minimising the time of
+// the busiest wave of a workgroup holding `tw` tiles.
+int pick_splits(int tw, int sc) {
+  int best = 1;
+  long best_t = -1;
+  for (int w = 1; w <= sc; ++w) {
+    if (sc % w) continue;
+    const long units = (long)tw * w;
+    const long t = ((units + kWaves - 1) / kWaves) * (sc / w);
+    if (best_t < 0 || t < best_t) {
+      best_t = t;
+      best = w;
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
+// Returns QW_ERR_UNSUPPORTED (nothing enqueued) when the shape does not fit
+// this kernel; the caller then uses the vector-ALU kernel.
+qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void *const *ys,
+                 bool f32, int cus, hipStream_t s) {
+  const int K = ws[0].K;
+  if (K % 512 != 0 || B < 1 || B > 8 || count > kMats) return QW_ERR_UNSUPPORTED;
+  if ((long)B * K > (long)kXItems * kThreads * 8) return QW_ERR_UNSUPPORTED;
+  int na_max = 0;
+  for (int i = 0; i < count; ++i) {
+    const int npad = ws[i].n_out > 0 ? ws[i].n_out_pad : 0;
+    if ((size_t)ws[i].N * npad * 2 >= (1ull << 31)) return QW_ERR_UNSUPPORTED;
+    na_max = max(na_max, (npad + kAnchorChunk - 1) / kAnchorChunk);
+  }
+  const int xo_len = na_max * kAnchorChunk;
+  if (xo_len > kIdxItems * kThreads) return QW_ERR_UNSUPPORTED;
+  const int SC = K / 512;
+  Args a{};
+  a.count = count;
+  a.x = x;
+  a.K = K;
+  a.f32out = f32 ? 1 : 0;
+  a.xo_len = xo_len;
+  // every matrix is planned as if it were launched alone (its workgroup
+  // count, hence its K split and summation order, do not depend on what it
+  // is grouped with), so a grouped launch gives the bits of separate ones
+  const char *wpc = getenv("QW_GEMV_MC_WG_PER_CU");
+  const int wgs_per_cu = wpc ? max(1, atoi(wpc)) : 1;
+  int grid = 0, units_max = 0;
+  for (int i = 0; i < count; ++i) {
+    Mat &m = a.m[i];
+    m.codes = reinterpret_cast<const uint32_t *>(ws[i].codes);
+    m.sz = reinterpret_cast<const uint32_t *>(ws[i].scales);
+    m.mask = ws[i].n_out > 0 ? ws[i].out_mask : nullptr;
+    m.idx = ws[i].out_idx;
+    m.wo = ws[i].out_w;
+    m.y = ys[i];
+    m.N = ws[i].N;
+    m.n_out = ws[i].n_out;
+    m.n_out_pad = ws[i].n_out > 0 ? ws[i].n_out_pad : 0;
+    m.tiles = (m.N + 15) / 16;
+    m.wg_count = max(1, min(m.tiles, cus * wgs_per_cu));
+    m.wg_begin = grid;
+    grid += m.wg_count;
+    const int tw = (m.tiles + m.wg_count - 1) / m.wg_count;
+    m.W = pick_splits(tw, SC);
+    units_max = max(units_max, tw * m.W);
+  }
+  a.units_max = units_max;
+  for (int i = 0; i < count; ++i)
+    if ((long)a.m[i].tiles * (a.m[i].wg_count + 1) >= (1L << 31)) return QW_ERR_UNSUPPORTED;
+  const size_t lds = lds_layout(B, K, xo_len, units_max).total;
+  if (lds > 160 * 1024) return QW_ERR_UNSUPPORTED;
+  return launch_b(a, B, grid, lds, s);
+}
+
+}  // namespace gemv2m
+}  // namespace qw

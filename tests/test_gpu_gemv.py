@@ -177,3 +177,25 @@ def test_timed_call_records_kernel_duration_and_same_result():
     qw.qgemv_2bit(pw, x, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert s.elapsed_time(e) == ms
+
+
+@pytest.mark.parametrize("N,K,n_anchor,B", [(2048, 2048, 0, 1), (13824, 5120, 179, 1), (1000, 5120, 179, 3),
+                                            (64, 3072, 40, 2), (300, 27648, 967, 1), (777, 4096, 0, 8),
+                                            (16, 512, 5, 6), (17, 1024, 3, 7)])
+def test_gemv_2bit_matrix_core_and_vector_paths(N, K, n_anchor, B, monkeypatch):
+    """Both kernels of qgemv_2bit (matrix-core path for K % 512 == 0 when
+    the shape fits it, vector-ALU path otherwise or when forced) against the
+    oracle on the same inputs."""
+    W = inputs.weight(N, K, workload=78)
+    rng = np.random.default_rng(N + K)
+    idx = np.sort(rng.choice(K, n_anchor, replace=False)).astype(np.int32) if n_anchor else None
+    x = inputs.act_f16(B, K, workload=78)
+    pw = _packed_2bit(W, idx)
+    ref = _ref_2bit(W, x, idx)
+    monkeypatch.setenv("QW_GEMV_VALU", "0")
+    y_mc = _run_2bit(pw, x, f32=True)
+    monkeypatch.setenv("QW_GEMV_VALU", "1")
+    y_va = _run_2bit(pw, x, f32=True)
+    e_mc, e_va = norm_err(y_mc, ref), norm_err(y_va, ref)
+    print(f"{N}x{K} anchors={n_anchor} B={B}: matrix-core err {e_mc:.3e}, vector err {e_va:.3e}")
+    assert e_mc <= TOL and e_va <= TOL
