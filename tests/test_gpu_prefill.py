@@ -37,7 +37,7 @@ FMTS = [qw.QW_FMT_2BIT_G32, qw.QW_FMT_NF4_B64]
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("M,N,K", [(300, 200, 512), (1, 1, 64), (257, 129, 128), (512, 1024, 2048)])
+@pytest.mark.parametrize("M,N,K", [(300, 200, 512), (1, 1, 64), (257, 129, 128), (512, 1024, 2048), (513, 300, 192), (64, 777, 64)])
 def test_prefill_small(fmt, M, N, K):
     import torch
     W = inputs.weight(N, K, workload=80)
