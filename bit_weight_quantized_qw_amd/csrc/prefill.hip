@@ -507,25 +507,40 @@ __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
           T[j][g][1] = pack_bf16x2(__builtin_fmaf(S, 0.45f, Z), __builtin_fmaf(S, 1.52f, Z));
         }
     }
-    bf16x8 fa[2][8];
+    // software pipeline: the A fragments and B fragments of slice kk+1 are
+    // read and dequantized while the 16 products of slice kk run
+    bf16x8 fa[2][8], fb[2][2];
     read_a(buf, 0, fa[0]);
+    fb[0][0] = make_b(wr[PAR], 0, 0, T);
+    fb[0][1] = make_b(wr[PAR], 1, 0, T);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      if (kk + 1 < BK / 16) read_a(buf, kk + 1, fa[(kk + 1) & 1]);
-      const bf16x8 b0 = make_b(wr[PAR], 0, kk, T);
-      const bf16x8 b1 = make_b(wr[PAR], 1, kk, T);
+      if (kk + 1 < BK / 16) {
+        read_a(buf, kk + 1, fa[(kk + 1) & 1]);
+        fb[(kk + 1) & 1][0] = make_b(wr[PAR], 0, kk + 1, T);
+        fb[(kk + 1) & 1][1] = make_b(wr[PAR], 1, kk + 1, T);
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], b0, acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], b1, acc[i][1], 0, 0, 0);
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][0], acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][1], acc[i][1], 0, 0, 0);
       }
       if (kk == 0) {
         store_x(buf ^ 1);
         load_x(kn2);
         load_w(kn1, wr[PAR ^ 1]);
       }
-      // keep each slice's reads, dequantization and products together
-      // (hoisting later slices' fragment reads would exceed the registers)
+      // 16 x {1 product, a few vector ops, a fragment read, an LDS write,
+      // a memory read}: the vector work runs while the products execute
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     // LDS-only barrier: the loads of the next steps stay in flight
