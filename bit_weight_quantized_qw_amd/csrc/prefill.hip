@@ -20,6 +20,8 @@
 // v_q = bf16(fma(S, C[q], Z)) are formed once and packed into two dwords;
 // a v_perm_b32 whose byte selectors are built from two code fields then
 // assembles a bf16 pair, so each weight costs a few integer ops.
+#include <stdlib.h>
+
 #include <type_traits>
 
 #include "qw_internal.h"
@@ -44,6 +46,7 @@ struct PrefillArgs {
   void *Y;                 // [M][N]
   int M, N, K, n_out, n_out_pad;
   int mt_count;            // number of 256-row tiles along M
+  int n_begin;             // first output column of this launch's tiles
   float nf4[16];
 };
 
@@ -361,7 +364,7 @@ __device__ inline __amdgpu_buffer_rsrc_t pf_rsrc(const void *p, uint32_t bytes) 
 }
 constexpr uint32_t kPfOob = 0x7FFFFFF0u;  // an offset always past a buffer's end
 
-template <int FMT, bool F32OUT>
+template <int FMT, bool F32OUT, int NJ>
 __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   // X [BM][LDA] x 2 buffers, then the NF4 table
@@ -373,7 +376,7 @@ __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
   const int b = blockIdx.x;
   const int m_tile = b % a.mt_count;
   const int n_tile = b / a.mt_count;
-  const int m0 = m_tile * BM, n0 = n_tile * BN;
+  const int m0 = m_tile * BM, n0 = a.n_begin + n_tile * (128 * NJ);
   const int K = a.K;
   const int KT = K / BK;
   const int hk = lane >> 5;  // which 8 of each 16-wide k slice this lane holds
@@ -411,27 +414,27 @@ __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
 
   // ---- W registers of this lane's two columns, two sets (step parity) ----
   constexpr int WR = FMT == QW_FMT_2BIT_G32 ? 6 : 9;  // dwords per column per step
-  uint32_t wr[2][2][WR];
-  int gcol[2];
-  bool cvalid[2];
+  uint32_t wr[2][NJ][WR];
+  int gcol[NJ];
+  bool cvalid[NJ];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    gcol[j] = n0 + wv * 64 + j * 32 + (lane & 31);
+  for (int j = 0; j < NJ; ++j) {
+    gcol[j] = n0 + wv * 32 * NJ + j * 32 + (lane & 31);
     cvalid[j] = gcol[j] < a.N;
   }
   const uint32_t cb = FMT == QW_FMT_2BIT_G32 ? (uint32_t)K / 4 : (uint32_t)K / 2;  // code bytes per column
   const uint32_t sb = FMT == QW_FMT_2BIT_G32 ? (uint32_t)K / 8 : (uint32_t)K / 16;  // scale bytes per column
   const auto rcode = pf_rsrc(a.codes, (uint32_t)((size_t)a.N * cb));
   const auto rscale = pf_rsrc(a.scales, (uint32_t)((size_t)a.N * sb));
-  uint32_t co[2], so[2];
+  uint32_t co[NJ], so[NJ];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < NJ; ++j) {
     co[j] = cvalid[j] ? (uint32_t)gcol[j] * cb : kPfOob;
     so[j] = cvalid[j] ? (uint32_t)gcol[j] * sb : kPfOob;
   }
-  auto load_w = [&](int kt, uint32_t (&dst)[2][WR]) {
+  auto load_w = [&](int kt, uint32_t (&dst)[NJ][WR]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       if (FMT == QW_FMT_2BIT_G32) {
         // 64 codes = 16 bytes, two S/Z words
         const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rcode, (int)co[j], kt * 16, 0);
@@ -450,11 +453,11 @@ __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
     }
   };
 
-  floatx16 acc[8][2];
+  floatx16 acc[8][NJ];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
@@ -466,7 +469,7 @@ __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
   };
 
   // B fragment of column j for k slice kk of the step held in w
-  auto make_b = [&](const uint32_t (&w)[2][WR], int j, int kk, const uint32_t (&T)[2][2][2]) {
+  auto make_b = [&](const uint32_t (&w)[NJ][WR], int j, int kk, const uint32_t (&T)[NJ][2][2]) {
     uint32_t o[4];
     if (FMT == QW_FMT_2BIT_G32) {
       const int g = kk >> 1;
@@ -494,10 +497,10 @@ __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
     constexpr int buf = PAR;  // kt has the parity of the register set
     const int kn1 = min(kt + 1, KT - 1), kn2 = kt + 2;
     // value tables of the two groups of each column (2-bit)
-    uint32_t T[2][2][2];
+    uint32_t T[NJ][2][2];
     if (FMT == QW_FMT_2BIT_G32) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
           const uint32_t szw = wr[PAR][j][4 + g];
@@ -509,32 +512,32 @@ __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
     }
     // software pipeline: the A fragments and B fragments of slice kk+1 are
     // read and dequantized while the 16 products of slice kk run
-    bf16x8 fa[2][8], fb[2][2];
+    bf16x8 fa[2][8], fb[2][NJ];
     read_a(buf, 0, fa[0]);
-    fb[0][0] = make_b(wr[PAR], 0, 0, T);
-    fb[0][1] = make_b(wr[PAR], 1, 0, T);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) fb[0][j] = make_b(wr[PAR], j, 0, T);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       if (kk + 1 < BK / 16) {
         read_a(buf, kk + 1, fa[(kk + 1) & 1]);
-        fb[(kk + 1) & 1][0] = make_b(wr[PAR], 0, kk + 1, T);
-        fb[(kk + 1) & 1][1] = make_b(wr[PAR], 1, kk + 1, T);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) fb[(kk + 1) & 1][j] = make_b(wr[PAR], j, kk + 1, T);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][0], acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][1], acc[i][1], 0, 0, 0);
-      }
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
       if (kk == 0) {
         store_x(buf ^ 1);
         load_x(kn2);
         load_w(kn1, wr[PAR ^ 1]);
       }
-      // 16 x {1 product, a few vector ops, a fragment read, an LDS write,
+      // 8 NJ x {1 product, a few vector ops, a fragment read, an LDS write,
       // a memory read}: the vector work runs while the products execute
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
+      for (int t = 0; t < 8 * NJ; ++t) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
@@ -577,12 +580,12 @@ __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
   //      stores drop rows past M and columns past N. ----
   const uint32_t esz = F32OUT ? 4u : 2u;
   const auto ry = pf_rsrc(a.Y, (uint32_t)((size_t)a.M * a.N * esz));
-  constexpr int SL = 68;  // floats per slab row
+  constexpr int SL = 32 * NJ + 4;  // floats per slab row
   float *const slab = reinterpret_cast<float *>(smem) + wv * 32 * SL;
   const bool vec = F32OUT ? (a.N % 4 == 0) : (a.N % 8 == 0);
   // read-back mapping: CW columns per lane, RP rows per pass
   constexpr int CW = F32OUT ? 4 : 8;
-  constexpr int LPR = 64 / CW;  // lanes per slab row
+  constexpr int LPR = 32 * NJ / CW;  // lanes per slab row
   constexpr int RP = 64 / LPR;
   // all lane-dependent epilogue addresses come from a copy of the lane index
   // the compiler cannot see through, so none of them is hoisted above the K
@@ -593,7 +596,7 @@ __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
   // LDS byte address of this lane's first write: row 4 * (lane >> 5), column lane & 31
   const uint32_t slab_w = (uint32_t)reinterpret_cast<uintptr_t>(slab) +
                           (uint32_t)((4 * (ln >> 5) * SL + (ln & 31)) * 4);
-  const int gc = n0 + wv * 64 + cc;
+  const int gc = n0 + wv * 32 * NJ + cc;
   static_assert(4 * 32 * SL * 4 <= 2 * BM * LDA * 2, "slabs fit in the X buffers");
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -601,7 +604,7 @@ __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
     // makes the compiler copy acc to vector registers first, and that copy
     // pushes the allocator into spilling inside the K loop
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
@@ -654,24 +657,64 @@ __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
   }
 }
 
+template <int FMT, bool F32, int NJ>
+qw_status launch_w(const PrefillArgs &a, int n_begin, int n_tiles, hipStream_t s) {
+  if (n_tiles <= 0) return QW_OK;
+  PrefillArgs b = a;
+  b.n_begin = n_begin;
+  const size_t lds = (size_t)2 * BM * LDA * 2 + (FMT == QW_FMT_NF4_B64 ? 256 * 8 : 0);
+  QW_HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_w_kernel<FMT, F32, NJ>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
+  QW_HIP_TRY(launch(prefill_w_kernel<FMT, F32, NJ>, a.mt_count * n_tiles, NT, lds, s, b));
+  return QW_OK;
+}
+
+// Column split between 256-wide tiles and 128-wide tiles for the last
+// columns: a whole number of rounds of wide tiles over the CUs, then one
+// short round of narrow ones instead of a half-empty round of wide ones.
+// Cost model in units of one wide-tile round; a narrow tile costs 0.55 of a
+// wide one (half the products, same fixed per-step work).
+int wide_column_tiles(int mt, int N, int cus) {
+  const int nt = (N + 255) / 256;
+  double best = 1e30;
+  int best_n = nt;
+  for (int n = nt; n >= 0; --n) {
+    const long wide = (long)mt * n;
+    const int rest = N - 256 * n;
+    const long narrow = rest > 0 ? (long)mt * ((rest + 127) / 128) : 0;
+    const double cost = (double)((wide + cus - 1) / cus) + 0.55 * (double)((narrow + cus - 1) / cus);
+    if (cost < best - 1e-9) {
+      best = cost;
+      best_n = n;
+    }
+  }
+  return best_n;
+}
+
 template <int FMT>
-qw_status launch_fmt(const PrefillArgs &a, bool f32, hipStream_t s) {
-  const int nt = (a.N + BN - 1) / BN;
-  const int grid = a.mt_count * nt;
+qw_status launch_fmt(const PrefillArgs &a, bool f32, int cus, hipStream_t s) {
   const size_t esz = f32 ? 4 : 2;
   const bool fits32 = (size_t)a.M * a.K * 2 < (1ull << 31) && (size_t)a.M * a.N * esz < (1ull << 31) &&
                       (size_t)a.N * (a.K / 2) < (1ull << 31);
   if (a.n_out == 0 && fits32) {  // W straight to registers
-    const size_t lds = (size_t)2 * BM * LDA * 2 + (FMT == QW_FMT_NF4_B64 ? 256 * 8 : 0);
-    const void *fn = f32 ? reinterpret_cast<const void *>(&prefill_w_kernel<FMT, true>)
-                         : reinterpret_cast<const void *>(&prefill_w_kernel<FMT, false>);
-    QW_HIP_TRY(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-    if (f32)
-      QW_HIP_TRY(launch(prefill_w_kernel<FMT, true>, grid, NT, lds, s, a));
-    else
-      QW_HIP_TRY(launch(prefill_w_kernel<FMT, false>, grid, NT, lds, s, a));
+    // QW_PREFILL_WIDE_TILES overrides the number of 256-wide column tiles
+    // (tests use it to run the 128-wide kernel on small shapes)
+    const int nt = (a.N + 255) / 256;
+    const char *ev = getenv("QW_PREFILL_WIDE_TILES");
+    const int nw = ev ? max(0, min(atoi(ev), nt)) : wide_column_tiles(a.mt_count, a.N, cus);
+    const int rest = a.N - 256 * nw;
+    const int nn = rest > 0 ? (rest + 127) / 128 : 0;
+    if (f32) {
+      QW_TRY((launch_w<FMT, true, 2>(a, 0, nw, s)));
+      QW_TRY((launch_w<FMT, true, 1>(a, 256 * nw, nn, s)));
+    } else {
+      QW_TRY((launch_w<FMT, false, 2>(a, 0, nw, s)));
+      QW_TRY((launch_w<FMT, false, 1>(a, 256 * nw, nn, s)));
+    }
     return QW_OK;
   }
+  const int nt = (a.N + BN - 1) / BN;
+  const int grid = a.mt_count * nt;
   const size_t lds = (size_t)2 * (BM + BN) * LDA * 2 + (FMT == QW_FMT_NF4_B64 ? 256 * 8 : 0);
   const void *fn = f32 ? reinterpret_cast<const void *>(&prefill_kernel<FMT, true>)
                        : reinterpret_cast<const void *>(&prefill_kernel<FMT, false>);
@@ -697,7 +740,8 @@ extern "C" qw_status qgemm_prefill(const qw_weight *w, const void *X, int M, voi
   if (st != QW_OK) return st;
   if (w->K % 64) return QW_ERR_UNSUPPORTED;
   if (!aligned16(X) || !aligned16(Y)) return QW_ERR_ALIGNMENT;
-  st = current_device(nullptr);
+  int cus = 0;
+  st = current_device(&cus);
   if (st != QW_OK) return st;
   PrefillArgs a{};
   a.X = reinterpret_cast<const uint16_t *>(X);
@@ -715,6 +759,6 @@ extern "C" qw_status qgemm_prefill(const qw_weight *w, const void *X, int M, voi
   const float *L = nf4_levels_host();
   for (int i = 0; i < 16; ++i) a.nf4[i] = L[i];
   const bool f32 = y_dtype == QW_DT_F32;
-  if (w->format == QW_FMT_2BIT_G32) return launch_fmt<QW_FMT_2BIT_G32>(a, f32, as_stream(stream));
-  return launch_fmt<QW_FMT_NF4_B64>(a, f32, as_stream(stream));
+  if (w->format == QW_FMT_2BIT_G32) return launch_fmt<QW_FMT_2BIT_G32>(a, f32, cus, as_stream(stream));
+  return launch_fmt<QW_FMT_NF4_B64>(a, f32, cus, as_stream(stream));
 }

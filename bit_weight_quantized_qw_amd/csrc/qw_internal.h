@@ -18,6 +18,13 @@ namespace qw {
     if (qw_e_ != hipSuccess) return QW_ERR_HIP;            \
   } while (0)
 
+// Returns a failed qw_status from the enclosing function.
+#define QW_TRY(expr)                                       \
+  do {                                                     \
+    qw_status qw_s_ = (expr);                              \
+    if (qw_s_ != QW_OK) return qw_s_;                      \
+  } while (0)
+
 // ---------------------------------------------------------------------------
 // Kernel launches and per-call timing (qw_time_next_call). Every entry point
 // that enqueues kernels opens a CallScope before validating its arguments;

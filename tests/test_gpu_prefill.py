@@ -36,10 +36,18 @@ def _run(pw, Xbits, f32=True):
 FMTS = [qw.QW_FMT_2BIT_G32, qw.QW_FMT_NF4_B64]
 
 
+SMALL = [(300, 200, 512), (1, 1, 64), (257, 129, 128), (512, 1024, 2048), (513, 300, 192), (64, 777, 64)]
+
+
+# wide=None: the library's own split between 256- and 128-wide column tiles;
+# "0": 128-wide tiles only; "1": one 256-wide column tile, the rest 128-wide
 @pytest.mark.parametrize("fmt", FMTS)
-@pytest.mark.parametrize("M,N,K", [(300, 200, 512), (1, 1, 64), (257, 129, 128), (512, 1024, 2048), (513, 300, 192), (64, 777, 64)])
-def test_prefill_small(fmt, M, N, K):
+@pytest.mark.parametrize("M,N,K", SMALL)
+@pytest.mark.parametrize("wide", [None, "0", "1"])
+def test_prefill_small(fmt, M, N, K, wide, monkeypatch):
     import torch
+    if wide is not None:
+        monkeypatch.setenv("QW_PREFILL_WIDE_TILES", wide)
     W = inputs.weight(N, K, workload=80)
     X = inputs.act_bf16_bits(M, K, workload=80)
     pw = _pack(W, fmt)
