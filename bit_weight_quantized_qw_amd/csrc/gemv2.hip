@@ -96,6 +96,9 @@ qw_status launch_slice(const qw_weight *ws, int count, const uint16_t *x, int Bk
   }
 }
 
+qw_status launch_valu(const qw_weight *ws, int count, const uint16_t *x, int B, void *const *ys,
+                      bool f32, int cus, hipStream_t s);
+
 qw_status launch(const qw_weight *ws, int count, const void *x, int B, void *const *ys,
                  qw_dtype dt, hipStream_t s) {
   if (!ws || count < 1 || count > kMaxMats || !x || !ys) return QW_ERR_INVALID_ARG;
@@ -113,27 +116,64 @@ qw_status launch(const qw_weight *ws, int count, const void *x, int B, void *con
   qw_status st = current_device(&cus);
   if (st != QW_OK) return st;
   const bool f32 = dt == QW_DT_F32;
-  const size_t esz = f32 ? 4 : 2;
   for (int i = 0; i < count; ++i) {
     // buffer offsets are 32-bit
     if ((size_t)ws[i].N * (ws[i].K / 4) >= (1ull << 31)) return QW_ERR_UNSUPPORTED;
   }
   // the matrix-core kernel takes the whole batch in one pass when the shape
   // fits it; otherwise batch rows go through vector-ALU kernels of width 4,
-  // 2 and 1 (e.g. 7 = 4 + 2 + 1),
-  // narrower when the x slice of a wider one does not fit
+  // 2 and 1 (e.g. 7 = 4 + 2 + 1).
   // Path choice (measured on MI355X): the matrix-core kernel for batches of
   // two or more; at batch 1 only for large matrices with K <= 8192, where it
   // is at least as fast. QW_GEMV_VALU=1 forces the vector-ALU kernel and
   // QW_GEMV_VALU=0 the matrix-core one where it applies (for tests).
-  long nk = 0;
-  for (int i = 0; i < count; ++i) nk += (long)ws[i].N * ws[i].K;
+  // The choice is made per matrix (a grouped call gives the bits of
+  // separate calls): the matrices that take the matrix-core kernel go out as
+  // one grouped launch of it (or one by one when the group does not fit it),
+  // the rest as grouped launches of the vector-ALU kernel.
   const int force = env_int("QW_GEMV_VALU", -1);
-  const bool mc = force == 0 || (force < 0 && (B >= 2 || (K <= 8192 && nk >= (16L << 20))));
-  if (mc) {
-    st = gemv2m::launch(ws, count, reinterpret_cast<const uint16_t *>(x), B, ys, f32, cus, s);
-    if (st != QW_ERR_UNSUPPORTED) return st;
+  qw_weight mc_w[kMaxMats], va_w[kMaxMats];
+  void *mc_y[kMaxMats], *va_y[kMaxMats];
+  int n_mc = 0, n_va = 0;
+  for (int i = 0; i < count; ++i) {
+    const long nk = (long)ws[i].N * ws[i].K;
+    const bool mc = force == 0 || (force < 0 && (B >= 2 || (K <= 8192 && nk >= (16L << 20))));
+    if (mc) {
+      mc_w[n_mc] = ws[i];
+      mc_y[n_mc++] = ys[i];
+    } else {
+      va_w[n_va] = ws[i];
+      va_y[n_va++] = ys[i];
+    }
   }
+  const uint16_t *xh = reinterpret_cast<const uint16_t *>(x);
+  if (n_mc > 0) {
+    st = gemv2m::launch(mc_w, n_mc, xh, B, mc_y, f32, cus, s);
+    if (st == QW_ERR_UNSUPPORTED) {
+      for (int i = 0; i < n_mc; ++i) {
+        st = gemv2m::launch(&mc_w[i], 1, xh, B, &mc_y[i], f32, cus, s);
+        if (st == QW_ERR_UNSUPPORTED) {
+          va_w[n_va] = mc_w[i];
+          va_y[n_va++] = mc_y[i];
+        } else if (st != QW_OK) {
+          return st;
+        }
+      }
+    } else if (st != QW_OK) {
+      return st;
+    }
+  }
+  if (n_va == 0) return QW_OK;
+  return launch_valu(va_w, n_va, xh, B, va_y, f32, cus, s);
+}
+
+// Vector-ALU kernels over the whole batch: slices of width 4, 2 and 1
+// (narrower when the x slice of a wider one does not fit).
+qw_status launch_valu(const qw_weight *ws, int count, const uint16_t *x, int B, void *const *ys,
+                      bool f32, int cus, hipStream_t s) {
+  const int K = ws[0].K;
+  const size_t esz = f32 ? 4 : 2;
+  qw_status st = QW_OK;
   int b0 = 0;
   while (b0 < B) {
     const int rest = B - b0;
@@ -147,8 +187,7 @@ qw_status launch(const qw_weight *ws, int count, const void *x, int B, void *con
     void *ysl[kMaxMats];
     for (int i = 0; i < count; ++i)
       ysl[i] = reinterpret_cast<char *>(ys[i]) + (size_t)b0 * ws[i].N * esz;
-    st = launch_slice(ws, count, reinterpret_cast<const uint16_t *>(x) + (size_t)b0 * K, Bk, ysl,
-                      f32, p, rpg, wgb, s);
+    st = launch_slice(ws, count, x + (size_t)b0 * K, Bk, ysl, f32, p, rpg, wgb, s);
     if (st != QW_OK) return st;
     b0 += Bk;
   }

@@ -353,8 +353,9 @@ __global__ __launch_bounds__(kThreads) void kernel(Args a) {
   //      unconditional, so the waits below count exactly) ----
   Cursor cl = st.start(wave);
   __builtin_amdgcn_sched_barrier(0);
+  constexpr int E = kEarly < P ? kEarly : P;
 #pragma unroll
-  for (int i = 0; i < kEarly; ++i) {
+  for (int i = 0; i < E; ++i) {
     issue(ring[i], cl);
     st.advance(cl);
   }
@@ -436,21 +437,23 @@ __global__ __launch_bounds__(kThreads) void kernel(Args a) {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 #pragma unroll
-  for (int i = kEarly; i < P; ++i) {
+  for (int i = E; i < P; ++i) {
     issue(ring[i], cl);
     st.advance(cl);
   }
 
   // anchor x gathered once (zero past n_out; indices clamped to the zeros
-  // at K), then a second LDS-only barrier
-  for (int o = threadIdx.x; o < a.xo_len; o += kThreads) {
-    const uint32_t ci = o < M.n_out ? min((uint32_t)aidx_l[o], (uint32_t)K) : (uint32_t)K;
+  // at K), then a second LDS-only barrier (none without anchors)
+  if (a.xo_len > 0) {  // uniform
+    for (int o = threadIdx.x; o < a.xo_len; o += kThreads) {
+      const uint32_t ci = o < M.n_out ? min((uint32_t)aidx_l[o], (uint32_t)K) : (uint32_t)K;
 #pragma unroll
-    for (int b = 0; b < B; ++b) xo[b * a.xo_len + o] = xraw[(size_t)b * KX + ci];
+      for (int b = 0; b < B; ++b) xo[b * a.xo_len + o] = xraw[(size_t)b * KX + ci];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
   // ---- per-lane A-operand addresses ----
   const int s_a = j >> 2, limb = j & 3;
@@ -546,12 +549,17 @@ __global__ __launch_bounds__(kThreads) void kernel(Args a) {
     }
   };
 
+  // Rounds of P steps: every round but the last refills each slot after
+  // consuming it (unconditionally, so the waits count exactly; a refill past
+  // the end reads through a zero-size descriptor); the last round only
+  // drains the ring, so at most P - 1 refills per wave are dead.
+  int n_steps = 0;
+  for (int u = wave; u < n_units; u += kWaves) n_steps += st.unit_len(u % st.W);
+  const int n_rounds = (n_steps + P - 1) / P;
   Cursor cc = st.start(wave);
-  while (cc.unit < n_units) {
+  for (int r = 1; r < n_rounds; ++r) {
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-      // consumers are conditional, the refill is not (past the end it reads
-      // through a zero-size descriptor), so every slot's loads stay in order
       const bool on = cc.unit < n_units;  // uniform
       const int u = cc.unit;
       const bool last = on && cc.step + 1 >= cc.len;
@@ -561,6 +569,15 @@ __global__ __launch_bounds__(kThreads) void kernel(Args a) {
       if (on) st.advance(cc);
       if (last) finish_unit(u);
     }
+  }
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const bool on = cc.unit < n_units;  // uniform
+    const int u = cc.unit;
+    const bool last = on && cc.step + 1 >= cc.len;
+    if (on) compute(ring[i], cc);
+    if (on) st.advance(cc);
+    if (last) finish_unit(u);
   }
 
   // ---- partial row sums of every unit -> y, splits added in order ----
@@ -601,16 +618,18 @@ qw_status launch_bp(const Args &a, int grid, size_t lds, hipStream_t s) {
   return a.count > 1 ? launch_bpm<B, P, true>(a, grid, lds, s) : launch_bpm<B, P, false>(a, grid, lds, s);
 }
 
-qw_status launch_b(const Args &a, int B, int grid, size_t lds, hipStream_t s) {
+// Ring depth: the deep ring (6 slots up to batch 2, 4 beyond) when waves
+// have that many steps, 3 otherwise (fewer dead prologue loads).
+qw_status launch_b(const Args &a, int B, bool deep, int grid, size_t lds, hipStream_t s) {
   switch (B) {
-    case 1: return launch_bp<1, 6>(a, grid, lds, s);
-    case 2: return launch_bp<2, 6>(a, grid, lds, s);
-    case 3: return launch_bp<3, 4>(a, grid, lds, s);
-    case 4: return launch_bp<4, 4>(a, grid, lds, s);
-    case 5: return launch_bp<5, 4>(a, grid, lds, s);
-    case 6: return launch_bp<6, 4>(a, grid, lds, s);
-    case 7: return launch_bp<7, 4>(a, grid, lds, s);
-    default: return launch_bp<8, 4>(a, grid, lds, s);
+    case 1: return deep ? launch_bp<1, 6>(a, grid, lds, s) : launch_bp<1, 3>(a, grid, lds, s);
+    case 2: return deep ? launch_bp<2, 6>(a, grid, lds, s) : launch_bp<2, 3>(a, grid, lds, s);
+    case 3: return deep ? launch_bp<3, 4>(a, grid, lds, s) : launch_bp<3, 3>(a, grid, lds, s);
+    case 4: return deep ? launch_bp<4, 4>(a, grid, lds, s) : launch_bp<4, 3>(a, grid, lds, s);
+    case 5: return deep ? launch_bp<5, 4>(a, grid, lds, s) : launch_bp<5, 3>(a, grid, lds, s);
+    case 6: return deep ? launch_bp<6, 4>(a, grid, lds, s) : launch_bp<6, 3>(a, grid, lds, s);
+    case 7: return deep ? launch_bp<7, 4>(a, grid, lds, s) : launch_bp<7, 3>(a, grid, lds, s);
+    default: return deep ? launch_bp<8, 4>(a, grid, lds, s) : launch_bp<8, 3>(a, grid, lds, s);
   }
 }
 
@@ -660,7 +679,7 @@ qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void 
   // is grouped with), so a grouped launch gives the bits of separate ones
   const char *wpc = getenv("QW_GEMV_MC_WG_PER_CU");
   const int wgs_per_cu = wpc ? max(1, atoi(wpc)) : 1;
-  int grid = 0, units_max = 0;
+  int grid = 0, units_max = 0, steps_max = 0;
   for (int i = 0; i < count; ++i) {
     Mat &m = a.m[i];
     m.codes = reinterpret_cast<const uint32_t *>(ws[i].codes);
@@ -679,13 +698,22 @@ qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void 
     const int tw = (m.tiles + m.wg_count - 1) / m.wg_count;
     m.W = pick_splits(tw, SC);
     units_max = max(units_max, tw * m.W);
+    // steps of the busiest wave (upper bound): units per wave times the
+    // longest unit (code steps plus anchor chunks of its split)
+    const int na = (m.n_out_pad + kAnchorChunk - 1) / kAnchorChunk;
+    steps_max = max(steps_max, ((tw * m.W + kWaves - 1) / kWaves) * (SC / m.W + (na + m.W - 1) / m.W));
   }
   a.units_max = units_max;
   for (int i = 0; i < count; ++i)
     if ((long)a.m[i].tiles * (a.m[i].wg_count + 1) >= (1L << 31)) return QW_ERR_UNSUPPORTED;
   const size_t lds = lds_layout(B, K, xo_len, units_max).total;
   if (lds > 160 * 1024) return QW_ERR_UNSUPPORTED;
-  return launch_b(a, B, grid, lds, s);
+  // QW_GEMV_MC_DEEP=0/1 forces the ring depth (tests check both give the
+  // same bits)
+  const int deep_p = B <= 2 ? 6 : 4;
+  const char *dv = getenv("QW_GEMV_MC_DEEP");
+  const bool deep = dv ? atoi(dv) != 0 : steps_max >= deep_p;
+  return launch_b(a, B, deep, grid, lds, s);
 }
 
 }  // namespace gemv2m

@@ -199,3 +199,24 @@ def test_gemv_2bit_matrix_core_and_vector_paths(N, K, n_anchor, B, monkeypatch):
     e_mc, e_va = norm_err(y_mc, ref), norm_err(y_va, ref)
     print(f"{N}x{K} anchors={n_anchor} B={B}: matrix-core err {e_mc:.3e}, vector err {e_va:.3e}")
     assert e_mc <= TOL and e_va <= TOL
+
+
+@pytest.mark.parametrize("N,K,n_anchor,B", [(1024, 5120, 179, 1), (2048, 2048, 0, 1), (11008, 4096, 0, 1),
+                                            (1000, 5120, 179, 3), (64, 3072, 40, 2)])
+def test_gemv_2bit_ring_depth_same_bits(N, K, n_anchor, B, monkeypatch):
+    """The matrix-core kernel's two ring depths (prefetch slots per wave)
+    change only when loads are issued, never the arithmetic: same bits."""
+    W = inputs.weight(N, K, workload=79)
+    rng = np.random.default_rng(N * 7 + K)
+    idx = np.sort(rng.choice(K, n_anchor, replace=False)).astype(np.int32) if n_anchor else None
+    x = inputs.act_f16(B, K, workload=79)
+    pw = _packed_2bit(W, idx)
+    monkeypatch.setenv("QW_GEMV_VALU", "0")
+    monkeypatch.setenv("QW_GEMV_MC_DEEP", "0")
+    y3 = _run_2bit(pw, x, f32=True)
+    monkeypatch.setenv("QW_GEMV_MC_DEEP", "1")
+    y6 = _run_2bit(pw, x, f32=True)
+    ref = _ref_2bit(W, x, idx)
+    print(f"{N}x{K} anchors={n_anchor} B={B}: shallow err {norm_err(y3, ref):.3e} deep err {norm_err(y6, ref):.3e} "
+          f"max |diff| {np.abs(y3 - y6).max():.3e}")
+    np.testing.assert_array_equal(y3, y6)
