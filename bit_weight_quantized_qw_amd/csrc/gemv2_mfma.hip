@@ -618,8 +618,7 @@ qw_status launch_bp(const Args &a, int grid, size_t lds, hipStream_t s) {
   return a.count > 1 ? launch_bpm<B, P, true>(a, grid, lds, s) : launch_bpm<B, P, false>(a, grid, lds, s);
 }
 
-// Ring depth: the deep ring (6 slots up to batch 2, 4 beyond) when waves
-// have that many steps, 3 otherwise (fewer dead prologue loads).
+// Ring depth: 3 slots, or the deep ring (6 slots up to batch 2, 4 beyond).
 qw_status launch_b(const Args &a, int B, bool deep, int grid, size_t lds, hipStream_t s) {
   switch (B) {
     case 1: return deep ? launch_bp<1, 6>(a, grid, lds, s) : launch_bp<1, 3>(a, grid, lds, s);
@@ -679,7 +678,7 @@ qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void 
   // is grouped with), so a grouped launch gives the bits of separate ones
   const char *wpc = getenv("QW_GEMV_MC_WG_PER_CU");
   const int wgs_per_cu = wpc ? max(1, atoi(wpc)) : 1;
-  int grid = 0, units_max = 0, steps_max = 0;
+  int grid = 0, units_max = 0;
   for (int i = 0; i < count; ++i) {
     Mat &m = a.m[i];
     m.codes = reinterpret_cast<const uint32_t *>(ws[i].codes);
@@ -698,21 +697,18 @@ qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void 
     const int tw = (m.tiles + m.wg_count - 1) / m.wg_count;
     m.W = pick_splits(tw, SC);
     units_max = max(units_max, tw * m.W);
-    // steps of the busiest wave (upper bound): units per wave times the
-    // longest unit (code steps plus anchor chunks of its split)
-    const int na = (m.n_out_pad + kAnchorChunk - 1) / kAnchorChunk;
-    steps_max = max(steps_max, ((tw * m.W + kWaves - 1) / kWaves) * (SC / m.W + (na + m.W - 1) / m.W));
   }
   a.units_max = units_max;
   for (int i = 0; i < count; ++i)
     if ((long)a.m[i].tiles * (a.m[i].wg_count + 1) >= (1L << 31)) return QW_ERR_UNSUPPORTED;
   const size_t lds = lds_layout(B, K, xo_len, units_max).total;
   if (lds > 160 * 1024) return QW_ERR_UNSUPPORTED;
-  // QW_GEMV_MC_DEEP=0/1 forces the ring depth (tests check both give the
+  // 3 ring slots per wave: measured on MI355X, the deep ring (6 slots up to
+  // batch 2, 4 beyond) is slower with weights coming from HBM even for waves
+  // with many steps; QW_GEMV_MC_DEEP=1 selects it (tests check both give the
   // same bits)
-  const int deep_p = B <= 2 ? 6 : 4;
   const char *dv = getenv("QW_GEMV_MC_DEEP");
-  const bool deep = dv ? atoi(dv) != 0 : steps_max >= deep_p;
+  const bool deep = dv ? atoi(dv) != 0 : false;
   return launch_b(a, B, deep, grid, lds, s);
 }
 

@@ -4,12 +4,13 @@
 //
 //   y[b][n] = sum_blk absmax[n][blk] * sum_{k in blk} x[b][k] L[q_k]
 //
-// Work split as in the 2-bit GEMV: a workgroup owns a block of rows; workers
-// of W waves walk sub-ranges and split K; lane l of wave w owns code dwords
-// u = (j*W + w)*64 + l (8 codes each) and keeps those x pairs in registers
-// (copied once per workgroup through LDS). Weights come in through buffer
-// loads; the first 2*RU rows are requested before anything else, then rows
-// stream through two register buffers.
+// Work split: a workgroup owns a block of rows; workers of W waves walk
+// sub-ranges and split K; lane l of wave w owns the half blocks
+// h = (j*W + w)*64 + l (32 codes = 16 bytes each, so every code load of a
+// wave reads 1 KB contiguous, plus the absmax of block h/2) and keeps those
+// x pairs in registers (copied once per workgroup through LDS). Rows stream through a ring of P row slots per wave;
+// every refill is unconditional (rows past the end read through a zero-size
+// descriptor) except in the last round, which only drains the ring.
 //
 // Decode: each code byte (two elements) indexes a 256-entry LDS table whose
 // entry holds the pair (L[lo], L[hi]) split into an fp16 high part and an
@@ -69,85 +70,79 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // Upper bound on the 16-byte x loads one thread issues while staging x
 // (the host checks ceil(B*K/8 / threads) against it).
 constexpr int kXLoads = 16;
+constexpr int kThreads = 512;
 
 // LDS: table uint2 [256] | x uint32 [B][K/2] | parts float [rows_per_wg][W][B]
-template <int B, int UW>
-__global__ __launch_bounds__(512) void gemv_nf4_kernel(ArgsNf4 a) {
-  // Both row buffers (2 loads per row and code dword) stay within the 63
-  // loads one wave can have outstanding, so the wait that precedes the x
-  // staging covers only the x loads.
-  constexpr int RU0 = 60 / (2 * 2 * UW);
-  constexpr int RU = RU0 < 1 ? 1 : (RU0 > 8 ? 8 : RU0);
+template <int B, int UW, int P>
+__global__ __launch_bounds__(kThreads) void gemv_nf4_kernel(ArgsNf4 a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
   uint2 *table = reinterpret_cast<uint2 *>(lds);
   uint32_t *xl = lds + 512;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
-  const int T = blockDim.x;
   const int W = a.W;
-  const int V = (T >> 6) / W;
+  const int V = (kThreads >> 6) / W;
   const int w = wave % W;
   const int K = a.K;
-  const int KD = K >> 3;   // code dwords per row (8 codes each)
-  const int KB = K >> 6;   // absmax per row
-  float *parts = reinterpret_cast<float *>(xl + B * (K >> 1));
+  const int NB = K >> 6;    // NF4 blocks per row
+  const int NH = K >> 5;    // half blocks per row
+  const int KP = K >> 1;    // x pairs per row
+  float *parts = reinterpret_cast<float *>(xl + B * KP);
   const int g0 = (int)blockIdx.x * a.rows_per_wg;
   const int g1 = min(a.N, g0 + a.rows_per_wg);
   const int rpw = (a.rows_per_wg + V - 1) / V;
   const int r0 = min(g1, g0 + (wave / W) * rpw);
   const int r1 = min(g1, r0 + rpw);
 
-  const auto rc = make_rsrc(a.codes, (uint32_t)((size_t)a.N * KD * 4));
-  const auto rm = make_rsrc(a.absmax, (uint32_t)((size_t)a.N * KB * 4));
-  uint32_t vc[UW], vm[UW];
+  const uint32_t row_cb = (uint32_t)K / 2, row_ab = (uint32_t)NB * 4;  // bytes per row
+  uint32_t vc[UW], va[UW];
 #pragma unroll
   for (int j = 0; j < UW; ++j) {
-    const int u = (j * W + w) * 64 + lane;
-    vc[j] = u < KD ? (uint32_t)u * 4 : kOob;
-    vm[j] = u < KD ? (uint32_t)(u >> 3) * 4 : kOob;
+    const int h = (j * W + w) * 64 + lane;
+    vc[j] = h < NH ? (uint32_t)h * 16 : kOob;
+    va[j] = h < NH ? (uint32_t)(h >> 1) * 4 : kOob;
   }
-  uint32_t cA[RU][UW], cB[RU][UW], mA[RU][UW], mB[RU][UW];
-  // Rows past the worker's range read through a zero-length descriptor, so
-  // every load is unconditional (no branch for the wait counters to merge).
-  const auto rz = make_rsrc(a.codes, 0u);
-  auto load = [&](uint32_t (&c)[RU][UW], uint32_t (&m)[RU][UW], int rb) {
+  struct Slot {
+    u32x4 c[UW];
+    uint32_t am[UW];
+  };
+  Slot ring[P];
+  const uint32_t n_cb = (uint32_t)((size_t)a.N * row_cb), n_ab = (uint32_t)((size_t)a.N * row_ab);
+  // rows past the worker's range read through zero-size descriptors
+  auto issue = [&](Slot &d, int rr) __attribute__((always_inline)) {
+    const bool ok = rr < r1;
+    const auto rc = make_rsrc(a.codes, ok ? n_cb : 0u);
+    const auto ra = make_rsrc(a.absmax, ok ? n_ab : 0u);
+    const uint32_t sc = ok ? (uint32_t)rr * row_cb : 0u, sa = ok ? (uint32_t)rr * row_ab : 0u;
 #pragma unroll
-    for (int i = 0; i < RU; ++i) {
-      const int rr = rb + i;
-      const bool ok = rr < r1;
-      const auto rcr = ok ? rc : rz, rmr = ok ? rm : rz;
-      const uint32_t so_c = ok ? (uint32_t)rr * KD * 4 : 0u, so_m = ok ? (uint32_t)rr * KB * 4 : 0u;
-#pragma unroll
-      for (int j = 0; j < UW; ++j) {
-        c[i][j] = bload(rcr, vc[j], so_c);
-        m[i][j] = bload(rmr, vm[j], so_m);
-      }
+    for (int j = 0; j < UW; ++j) {
+      d.c[j] = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)vc[j], (int)sc, 0);
+      d.am[j] = bload(ra, va[j], sa);
     }
   };
 
   // This group's copy of x: 16-byte buffer loads issued ahead of the weight
   // prefetch, so the LDS stores below wait only for them.
   const auto rx = make_rsrc(a.x, (uint32_t)((size_t)B * K * 2));
-  const int nx = (B * KD + T - 1) / T;  // uniform trip count
-  constexpr int XMAX = kXLoads;
-  u32x4 xv[XMAX];
+  const int nx = (B * (K >> 3) + kThreads - 1) / kThreads;  // uniform trip count
+  u32x4 xv[kXLoads];
 #pragma unroll
-  for (int q = 0; q < XMAX; ++q) {
+  for (int q = 0; q < kXLoads; ++q) {
     if (q < nx) {
-      const int i = q * T + (int)threadIdx.x;
-      xv[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, i < B * KD ? i * 16 : (int)kOob, 0, 0);
+      const int i = q * kThreads + (int)threadIdx.x;
+      xv[q] = __builtin_amdgcn_raw_buffer_load_b128(rx, i < B * (K >> 3) ? i * 16 : (int)kOob, 0, 0);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  load(cA, mA, r0);
-  load(cB, mB, r0 + RU);
+#pragma unroll
+  for (int i = 0; i < P; ++i) issue(ring[i], r0 + i);
   __builtin_amdgcn_sched_barrier(0);
 
   // level-pair table
   // (levels picked by a select chain over scalar kernel arguments: a
   // per-lane indexed read of the argument block would be a memory load
   // queued behind the weight prefetch)
-  for (int v = threadIdx.x; v < 256; v += T) {
+  for (int v = threadIdx.x; v < 256; v += kThreads) {
     const int q0 = v & 15, q1 = v >> 4;
     uint32_t h0 = a.L.hi[0], l0 = a.L.lo[0], h1 = a.L.hi[0], l1 = a.L.lo[0];
 #pragma unroll
@@ -163,84 +158,102 @@ __global__ __launch_bounds__(512) void gemv_nf4_kernel(ArgsNf4 a) {
     table[v] = e;
   }
 #pragma unroll
-  for (int q = 0; q < XMAX; ++q) {
-    const int i = q * T + (int)threadIdx.x;
-    if (q < nx && i < B * KD) reinterpret_cast<u32x4 *>(xl)[i] = xv[q];
+  for (int q = 0; q < kXLoads; ++q) {
+    const int i = q * kThreads + (int)threadIdx.x;
+    if (q < nx && i < B * (K >> 3)) reinterpret_cast<u32x4 *>(xl)[i] = xv[q];
   }
   // LDS-only barrier: a full __syncthreads would also drain the prefetch.
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
-  uint32_t xr[UW][B][4];
+  // x pairs of this lane's half blocks (zeros past the row end)
+  u32x4 xr[UW][B][4];
 #pragma unroll
   for (int j = 0; j < UW; ++j) {
-    const int u = (j * W + w) * 64 + lane;
+    const int h = (j * W + w) * 64 + lane;
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (u < KD) v = reinterpret_cast<const u32x4 *>(xl)[b * KD + u];
-      xr[j][b][0] = v[0]; xr[j][b][1] = v[1]; xr[j][b][2] = v[2]; xr[j][b][3] = v[3];
-    }
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (h < NH) v = reinterpret_cast<const u32x4 *>(xl + b * KP + h * 16)[q];
+        xr[j][b][q] = v;
+      }
   }
 
-  auto compute = [&](const uint32_t (&c)[RU][UW], const uint32_t (&m)[RU][UW], int rb) {
+  // four independent accumulator chains per part (high, remainder) so the
+  // dot products of one row do not wait on each other
+  auto compute = [&](const Slot &sl, int rr) __attribute__((always_inline)) {
+    float acc[B];
 #pragma unroll
-    for (int i = 0; i < RU; ++i) {
-      const int rr = rb + i;
-      if (rr >= r1) break;
-      float acc[B];
+    for (int b = 0; b < B; ++b) acc[b] = 0.0f;
 #pragma unroll
-      for (int b = 0; b < B; ++b) acc[b] = 0.0f;
+    for (int j = 0; j < UW; ++j) {
+      float th[B][4], tl[B][4];
 #pragma unroll
-      for (int j = 0; j < UW; ++j) {
-        const uint32_t cw = c[i][j];
-        uint2 e[4];
-        e[0] = table[cw & 0xFFu];
-        e[1] = table[(cw >> 8) & 0xFFu];
-        e[2] = table[(cw >> 16) & 0xFFu];
-        e[3] = table[cw >> 24];
-        const float am = __builtin_bit_cast(float, m[i][j]);
+      for (int b = 0; b < B; ++b)
 #pragma unroll
-        for (int b = 0; b < B; ++b) {
-          float t = 0.0f;
+        for (int c = 0; c < 4; ++c) th[b][c] = tl[b][c] = 0.0f;
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            t = dot2(xr[j][b][p], e[p].x, t);
-            t = dot2(xr[j][b][p], e[p].y, t);
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t cw = sl.c[j][d];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint2 e = table[(cw >> (8 * k)) & 0xFFu];
+#pragma unroll
+          for (int b = 0; b < B; ++b) {
+            const uint32_t xp = xr[j][b][d][k];
+            th[b][k] = dot2(xp, e.x, th[b][k]);
+            tl[b][k] = dot2(xp, e.y, tl[b][k]);
           }
-          acc[b] = __builtin_fmaf(am, t, acc[b]);
         }
       }
+      const float am = __builtin_bit_cast(float, sl.am[j]);
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        const float v = wave_sum_to_lane63(acc[b]);
-        if (lane == 63) {
-          if (W == 1) {
-            const size_t off = (size_t)b * a.N + rr;
-            if (a.f32out)
-              reinterpret_cast<float *>(a.y)[off] = v;
-            else
-              reinterpret_cast<_Float16 *>(a.y)[off] = (_Float16)v;
-          } else {
-            parts[((rr - g0) * W + w) * B + b] = v;
-          }
+        const float t = ((th[b][0] + th[b][1]) + (th[b][2] + th[b][3])) +
+                        ((tl[b][0] + tl[b][1]) + (tl[b][2] + tl[b][3]));
+        acc[b] = __builtin_fmaf(am, t, acc[b]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const float v = wave_sum_to_lane63(acc[b]);
+      if (lane == 63) {
+        if (W == 1) {
+          const size_t off = (size_t)b * a.N + rr;
+          if (a.f32out)
+            reinterpret_cast<float *>(a.y)[off] = v;
+          else
+            reinterpret_cast<_Float16 *>(a.y)[off] = (_Float16)v;
+        } else {
+          parts[((rr - g0) * W + w) * B + b] = v;
         }
       }
     }
   };
 
-  for (int r = r0; r < r1; r += 2 * RU) {
-    compute(cA, mA, r);
-    load(cA, mA, r + 2 * RU);
-    compute(cB, mB, r + RU);
-    load(cB, mB, r + 3 * RU);
+  // rounds of P rows; all but the last refill each slot after using it
+  const int n_rows = r1 - r0;
+  const int n_rounds = (n_rows + P - 1) / P;
+  int r = r0;
+  for (int rd = 1; rd < n_rounds; ++rd) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      compute(ring[i], r + i);
+      issue(ring[i], r + i + P);
+    }
+    r += P;
   }
+#pragma unroll
+  for (int i = 0; i < P; ++i)
+    if (r + i < r1) compute(ring[i], r + i);
 
   if (W > 1) {
     __syncthreads();
     const int nrows = g1 - g0;
-    for (int t = threadIdx.x; t < nrows * B; t += T) {
+    for (int t = threadIdx.x; t < nrows * B; t += kThreads) {
       const int rl = t / B, b = t - rl * B;
       float v = 0.0f;
       for (int i = 0; i < W; ++i) v += parts[(rl * W + i) * B + b];
@@ -253,37 +266,30 @@ __global__ __launch_bounds__(512) void gemv_nf4_kernel(ArgsNf4 a) {
   }
 }
 
-template <int B, int UW>
-qw_status launch_uw(const ArgsNf4 &a, int grid, int threads, size_t lds, hipStream_t s) {
+template <int B, int UW, int P>
+qw_status launch_k(const ArgsNf4 &a, int grid, size_t lds, hipStream_t s) {
   if (lds > 64 * 1024) {
-    QW_HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_nf4_kernel<B, UW>),
+    QW_HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(&gemv_nf4_kernel<B, UW, P>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
   }
-  QW_HIP_TRY(launch(gemv_nf4_kernel<B, UW>, grid, threads, lds, s, a));
+  QW_HIP_TRY(launch(gemv_nf4_kernel<B, UW, P>, grid, kThreads, lds, s, a));
   return QW_OK;
 }
 
-template <int B>
-qw_status launch_b(const ArgsNf4 &a, int UW, int grid, int threads, size_t lds, hipStream_t s) {
-  if constexpr (B == 1) {
-    if (UW <= 1) return launch_uw<1, 1>(a, grid, threads, lds, s);
-    if (UW <= 2) return launch_uw<1, 2>(a, grid, threads, lds, s);
-    if (UW <= 4) return launch_uw<1, 4>(a, grid, threads, lds, s);
-    if (UW <= 6) return launch_uw<1, 6>(a, grid, threads, lds, s);
-    if (UW <= 8) return launch_uw<1, 8>(a, grid, threads, lds, s);
-    if (UW <= 12) return launch_uw<1, 12>(a, grid, threads, lds, s);
-    return launch_uw<1, 16>(a, grid, threads, lds, s);
-  } else if constexpr (B == 2) {
-    if (UW <= 1) return launch_uw<2, 1>(a, grid, threads, lds, s);
-    if (UW <= 2) return launch_uw<2, 2>(a, grid, threads, lds, s);
-    if (UW <= 4) return launch_uw<2, 4>(a, grid, threads, lds, s);
-    if (UW <= 6) return launch_uw<2, 6>(a, grid, threads, lds, s);
-    return launch_uw<2, 8>(a, grid, threads, lds, s);
-  } else {
-    if (UW <= 1) return launch_uw<4, 1>(a, grid, threads, lds, s);
-    if (UW <= 2) return launch_uw<4, 2>(a, grid, threads, lds, s);
-    return launch_uw<4, 4>(a, grid, threads, lds, s);
+template <int B, int UW>
+qw_status launch_p(const ArgsNf4 &a, bool deep, int grid, size_t lds, hipStream_t s) {
+  return deep ? launch_k<B, UW, 6>(a, grid, lds, s) : launch_k<B, UW, 3>(a, grid, lds, s);
+}
+
+qw_status launch_b(const ArgsNf4 &a, int B, int UW, bool deep, int grid, size_t lds, hipStream_t s) {
+  if (B == 1) {
+    if (UW == 1) return launch_p<1, 1>(a, deep, grid, lds, s);
+    if (UW == 2) return launch_p<1, 2>(a, deep, grid, lds, s);
+    if (UW == 3) return launch_p<1, 3>(a, deep, grid, lds, s);
+    return launch_p<1, 4>(a, deep, grid, lds, s);
   }
+  if (B == 2) return UW == 1 ? launch_p<2, 1>(a, deep, grid, lds, s) : launch_p<2, 2>(a, deep, grid, lds, s);
+  return launch_p<4, 1>(a, deep, grid, lds, s);
 }
 
 int env_int(const char *name, int dflt) {
@@ -321,28 +327,30 @@ extern "C" qw_status qgemv_nf4(const qw_weight *w, const void *x, int B, void *y
   const bool f32 = y_dtype == QW_DT_F32;
   const size_t esz = f32 ? 4 : 2;
   const int K = w->K;
-  const int KD = K / 8;
-  const int U = (KD + 63) / 64;
+  const int NH = K / 32;  // half blocks per row
   static const Nf4Split sp = split_levels();
   if ((size_t)w->N * (K / 2) >= (1ull << 31)) return QW_ERR_UNSUPPORTED;
   int b0 = 0;
   while (b0 < B) {
     const int rest = B - b0;
     int Bk = rest >= 4 ? 4 : (rest >= 2 ? 2 : 1);
-    auto maxuw = [](int b) { return b == 1 ? 12 : (b == 2 ? 8 : 4); };
-    int W = 0, UW = 0, rpg = 0, grid = 0, threads = 0;
+    int W = 0, UW = 0, rpg = 0, grid = 0, rpw = 0;
     size_t lds = 0;
     for (;;) {
-      W = (U + maxuw(Bk) - 1) / maxuw(Bk);
-      UW = (U + W - 1) / W;
+      // half blocks per lane: 4 at batch 1, 2 at batch 2, else 1 (x pairs and
+      // the ring stay in registers); W, a power of two, waves split each row
+      const int maxuw = Bk == 1 ? 4 : (Bk == 2 ? 2 : 1);
+      W = 1;
+      while (W < 8 && W * 64 * maxuw < NH) W *= 2;
+      UW = (NH + 64 * W - 1) / (64 * W);
       const int V = 8 / W;
-      threads = 64 * W * V;
       const long target_wgs = max(1L, (long)cus * env_int("QW_GEMV_WG_PER_CU", 1));
       rpg = env_int("QW_GEMV_ROWS_PER_WG", 0);
       if (rpg <= 0) rpg = (int)max(1L, ((long)w->N + target_wgs - 1) / target_wgs);
       grid = (w->N + rpg - 1) / rpg;
+      rpw = (rpg + V - 1) / V;
       lds = 256 * 8 + (size_t)Bk * K * 2 + (W > 1 ? 4 * (size_t)rpg * W * Bk : 0);
-      if (W <= 8 && lds <= 160 * 1024 && (Bk * KD + threads - 1) / threads <= kXLoads) break;
+      if (UW <= maxuw && lds <= 160 * 1024 && (Bk * (K / 8) + kThreads - 1) / kThreads <= kXLoads) break;
       if (Bk == 1) return QW_ERR_UNSUPPORTED;
       Bk >>= 1;
     }
@@ -357,11 +365,12 @@ extern "C" qw_status qgemv_nf4(const qw_weight *w, const void *x, int B, void *y
     a.W = W;
     a.f32out = f32 ? 1 : 0;
     a.L = sp;
-    switch (Bk) {
-      case 1: st = launch_b<1>(a, UW, grid, threads, lds, as_stream(stream)); break;
-      case 2: st = launch_b<2>(a, UW, grid, threads, lds, as_stream(stream)); break;
-      default: st = launch_b<4>(a, UW, grid, threads, lds, as_stream(stream)); break;
-    }
+    // 3 row slots per wave: measured on MI355X, 6 slots (all rows of a wave
+    // in flight at once) are slower with weights coming from HBM;
+    // QW_GEMV_NF4_DEEP=1 selects them (tests check both give the same bits)
+    const char *dv = getenv("QW_GEMV_NF4_DEEP");
+    const bool deep = dv ? atoi(dv) != 0 : false;
+    st = launch_b(a, Bk, UW, deep, grid, lds, as_stream(stream));
     if (st != QW_OK) return st;
     b0 += Bk;
   }

@@ -220,3 +220,21 @@ def test_gemv_2bit_ring_depth_same_bits(N, K, n_anchor, B, monkeypatch):
     print(f"{N}x{K} anchors={n_anchor} B={B}: shallow err {norm_err(y3, ref):.3e} deep err {norm_err(y6, ref):.3e} "
           f"max |diff| {np.abs(y3 - y6).max():.3e}")
     np.testing.assert_array_equal(y3, y6)
+
+
+@pytest.mark.parametrize("N,K,B", [(11008, 4096, 1), (4096, 11008, 1), (300, 27648, 2), (1000, 4096, 4), (77, 640, 1)])
+def test_gemv_nf4_ring_depth_same_bits(N, K, B, monkeypatch):
+    """NF4 GEMV with 3 and 6 row slots per wave: same bits, and within the
+    tolerance of the oracle."""
+    W = inputs.weight(N, K, workload=82)
+    x = inputs.act_f16(B, K, workload=82)
+    q, a = oracle.quantize_nf4(W)
+    ref = oracle.gemv_nf4_ref(x, q, a)
+    monkeypatch.setenv("QW_GEMV_NF4_DEEP", "0")
+    y3 = _run_nf4(W, x, f32=True)
+    monkeypatch.setenv("QW_GEMV_NF4_DEEP", "1")
+    y6 = _run_nf4(W, x, f32=True)
+    e = norm_err(y3, ref)
+    print(f"NF4 {N}x{K} B={B}: err {e:.3e} max |diff| {np.abs(y3 - y6).max():.3e}")
+    assert e <= TOL
+    np.testing.assert_array_equal(y3, y6)
