@@ -657,7 +657,6 @@ qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void 
                  bool f32, int cus, hipStream_t s) {
   const int K = ws[0].K;
   if (K % 512 != 0 || B < 1 || B > 8 || count > kMats) return QW_ERR_UNSUPPORTED;
-  if ((long)B * K > (long)kXItems * kThreads * 8) return QW_ERR_UNSUPPORTED;
   int na_max = 0;
   for (int i = 0; i < count; ++i) {
     const int npad = ws[i].n_out > 0 ? ws[i].n_out_pad : 0;
@@ -701,15 +700,38 @@ qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void 
   a.units_max = units_max;
   for (int i = 0; i < count; ++i)
     if ((long)a.m[i].tiles * (a.m[i].wg_count + 1) >= (1L << 31)) return QW_ERR_UNSUPPORTED;
-  const size_t lds = lds_layout(B, K, xo_len, units_max).total;
-  if (lds > 160 * 1024) return QW_ERR_UNSUPPORTED;
+  // Widest batch slice whose x (limbs in LDS, raw x in the prologue
+  // registers) fits. Batch rows are independent (each is its own row of the
+  // product's A operand), so slicing changes no bits; it pays while slices
+  // hold at least two rows (a pass per single row is slower than the
+  // vector-ALU kernel).
+  auto fits = [&](int b) {
+    return (long)b * K <= (long)kXItems * kThreads * 8 &&
+           lds_layout(b, K, xo_len, units_max).total <= 160 * 1024;
+  };
+  int bmax = B;
+  while (bmax > 0 && !fits(bmax)) --bmax;
+  if (bmax < B && bmax < 2) return QW_ERR_UNSUPPORTED;
+  const int n_slices = (B + bmax - 1) / bmax;
   // 3 ring slots per wave: measured on MI355X, the deep ring (6 slots up to
   // batch 2, 4 beyond) is slower with weights coming from HBM even for waves
   // with many steps; QW_GEMV_MC_DEEP=1 selects it (tests check both give the
   // same bits)
   const char *dv = getenv("QW_GEMV_MC_DEEP");
   const bool deep = dv ? atoi(dv) != 0 : false;
-  return launch_b(a, B, deep, grid, lds, s);
+  const size_t esz = f32 ? 4 : 2;
+  int b0 = 0;
+  for (int sl = 0; sl < n_slices; ++sl) {
+    const int bs = (B - b0 + (n_slices - sl) - 1) / (n_slices - sl);  // balanced slices
+    Args as = a;
+    as.x = x + (size_t)b0 * K;
+    for (int i = 0; i < count; ++i)
+      as.m[i].y = reinterpret_cast<char *>(ys[i]) + (size_t)b0 * ws[i].N * esz;
+    const size_t lds = lds_layout(bs, K, xo_len, units_max).total;
+    QW_TRY(launch_b(as, bs, deep, grid, lds, s));
+    b0 += bs;
+  }
+  return QW_OK;
 }
 
 }  // namespace gemv2m
