@@ -124,8 +124,8 @@ qw_status launch(const qw_weight *ws, int count, const void *x, int B, void *con
   // fits it; otherwise batch rows go through vector-ALU kernels of width 4,
   // 2 and 1 (e.g. 7 = 4 + 2 + 1).
   // Path choice (measured on MI355X): the matrix-core kernel for batches of
-  // two or more; at batch 1 only for large matrices with K <= 8192, where it
-  // is at least as fast. QW_GEMV_VALU=1 forces the vector-ALU kernel and
+  // two or more, and at batch 1 for K <= 8192 (beyond, the vector-ALU kernel
+  // is faster at batch 1). QW_GEMV_VALU=1 forces the vector-ALU kernel and
   // QW_GEMV_VALU=0 the matrix-core one where it applies (for tests).
   // The choice is made per matrix (a grouped call gives the bits of
   // separate calls): the matrices that take the matrix-core kernel go out as
@@ -136,8 +136,7 @@ qw_status launch(const qw_weight *ws, int count, const void *x, int B, void *con
   void *mc_y[kMaxMats], *va_y[kMaxMats];
   int n_mc = 0, n_va = 0;
   for (int i = 0; i < count; ++i) {
-    const long nk = (long)ws[i].N * ws[i].K;
-    const bool mc = force == 0 || (force < 0 && (B >= 2 || (K <= 8192 && nk >= (16L << 20))));
+    const bool mc = force == 0 || (force < 0 && (B >= 2 || K <= 8192));
     if (mc) {
       mc_w[n_mc] = ws[i];
       mc_y[n_mc++] = ys[i];
