@@ -47,6 +47,7 @@ struct PrefillArgs {
   int M, N, K, n_out, n_out_pad;
   int mt_count;            // number of 256-row tiles along M
   int n_begin;             // first output column of this launch's tiles
+  int xcd_group;           // row tiles per group of the XCD-aware tile order (0: plain order)
   float nf4[16];
 };
 
@@ -359,13 +360,42 @@ __device__ inline void dequant8_2bit(uint32_t c, int h, uint32_t T0, uint32_t T1
   }
 }
 
+// Tile of workgroup b for an mt x nt grid of output tiles, XCD-aware.
+// Workgroups are dealt to the 8 XCDs round-robin (b % 8), each XCD with its
+// own L2. The q-th workgroup of XCD x takes tile t = (start of x's share) + q
+// of an order that walks groups of up to 4 row tiles column by column, so
+// the workgroups one XCD runs at a time cover a few row tiles times several
+// column tiles: each W column tile is fetched once per XCD for the row tiles
+// sharing it, instead of once per row tile (row tiles on different XCDs).
+// A bijection for every grid size.
+__device__ inline void xcd_tile(int b, int mt, int nt, int gmax, int &m_tile, int &n_tile) {
+  if (gmax <= 0) {  // plain order: row tile fastest
+    m_tile = b % mt;
+    n_tile = b / mt;
+    return;
+  }
+  constexpr int kXcds = 8;
+  const int total = mt * nt;
+  const int xcd = b % kXcds, q = b / kXcds;
+  const int per = total / kXcds, rem = total % kXcds;
+  const int t = xcd < rem ? xcd * (per + 1) + q : rem * (per + 1) + (xcd - rem) * per + q;
+  const int gm = mt < gmax ? mt : gmax;   // row tiles per group
+  const int g = t / (gm * nt);            // group of row tiles
+  const int rows_g = min(gm, mt - g * gm);  // the last group may be narrower
+  const int w = t - g * gm * nt;
+  m_tile = g * gm + w % rows_g;
+  n_tile = w / rows_g;
+}
+
 __device__ inline __amdgpu_buffer_rsrc_t pf_rsrc(const void *p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
 }
 constexpr uint32_t kPfOob = 0x7FFFFFF0u;  // an offset always past a buffer's end
 
-template <int FMT, bool F32OUT, int NJ>
-__global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
+template <int FMT, bool F32OUT, int NJ, int WM>
+__global__ __launch_bounds__(256 * WM) void prefill_w_kernel(PrefillArgs a) {
+  constexpr int NTW = 256 * WM;  // threads: WM x 4 waves
+  constexpr int IM = 8 / WM;     // 32-row blocks per wave
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   // X [BM][LDA] x 2 buffers, then the NF4 table
   float2 *ltab = reinterpret_cast<float2 *>(smem + 2 * BM * LDA);    // NF4 [256]
@@ -373,28 +403,28 @@ __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = blockIdx.x;
-  const int m_tile = b % a.mt_count;
-  const int n_tile = b / a.mt_count;
+  const int wm = wv >> 2, wn = wv & 3;  // wave's row half (WM = 2) and column quarter
+  int m_tile, n_tile;
+  xcd_tile((int)blockIdx.x, a.mt_count, (int)gridDim.x / a.mt_count, a.xcd_group, m_tile, n_tile);
   const int m0 = m_tile * BM, n0 = a.n_begin + n_tile * (128 * NJ);
   const int K = a.K;
   const int KT = K / BK;
   const int hk = lane >> 5;  // which 8 of each 16-wide k slice this lane holds
 
   if (FMT == QW_FMT_NF4_B64) {
-    for (int v = tid; v < 256; v += NT) ltab[v] = make_float2(a.nf4[v & 15], a.nf4[v >> 4]);
+    for (int v = tid; v < 256; v += NTW) ltab[v] = make_float2(a.nf4[v & 15], a.nf4[v >> 4]);
   }
 
-  // ---- X prefetch registers (8 x 16 bytes per thread per step) ----
-  // thread t copies 16-byte piece (t & 7) of rows (t >> 3) + 32 i, i < 8
+  // ---- X prefetch registers (IM x 16 bytes per thread per step) ----
+  // thread t copies 16-byte piece (t & 7) of rows (t >> 3) + 32 WM i, i < IM
   // (buffer loads: rows past M read through an out-of-range offset as 0)
-  u32x4 ra[8];
+  u32x4 ra[IM];
   const int xr = tid >> 3, xc = (tid & 7) * 8;
   const auto rx = pf_rsrc(a.X, (uint32_t)((size_t)a.M * K * 2));
-  uint32_t xo[8];
+  uint32_t xo[IM];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int gm = m0 + xr + 32 * i;
+  for (int i = 0; i < IM; ++i) {
+    const int gm = m0 + xr + 32 * WM * i;
     xo[i] = gm < a.M ? (uint32_t)(((size_t)gm * K + xc) * 2) : kPfOob;
   }
   // tiles at or past KT read as zeros (see the K loop below)
@@ -402,14 +432,14 @@ __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
     const bool live = kt < KT;
     const uint32_t k0b = live ? (uint32_t)kt * BK * 2 : 0u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < IM; ++i)
       ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(live ? xo[i] : kPfOob), (int)k0b, 0);
   };
-  uint16_t *const xs = smem + xr * LDA + xc;  // + buf * BM * LDA + 32 i * LDA
+  uint16_t *const xs = smem + xr * LDA + xc;  // + buf * BM * LDA + 32 WM i * LDA
   auto store_x = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4 *>(xs + buf * BM * LDA + 32 * i * LDA) = ra[i];
+    for (int i = 0; i < IM; ++i)
+      *reinterpret_cast<u32x4 *>(xs + buf * BM * LDA + 32 * WM * i * LDA) = ra[i];
   };
 
   // ---- W registers of this lane's two columns, two sets (step parity) ----
@@ -419,7 +449,7 @@ __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
   bool cvalid[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    gcol[j] = n0 + wv * 32 * NJ + j * 32 + (lane & 31);
+    gcol[j] = n0 + wn * 32 * NJ + j * 32 + (lane & 31);
     cvalid[j] = gcol[j] < a.N;
   }
   const uint32_t cb = FMT == QW_FMT_2BIT_G32 ? (uint32_t)K / 4 : (uint32_t)K / 2;  // code bytes per column
@@ -453,18 +483,18 @@ __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
     }
   };
 
-  floatx16 acc[8][NJ];
+  floatx16 acc[IM][NJ];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < IM; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const uint16_t *const ar = smem + (lane & 31) * LDA + hk * 8;  // + buf, i, kk offsets
-  auto read_a = [&](int buf, int kk, bf16x8 (&af)[8]) {
+  const uint16_t *const ar = smem + (wm * (BM / WM) + (lane & 31)) * LDA + hk * 8;  // + buf, i, kk offsets
+  auto read_a = [&](int buf, int kk, bf16x8 (&af)[IM]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < IM; ++i)
       af[i] = *reinterpret_cast<const bf16x8 *>(ar + buf * BM * LDA + 32 * i * LDA + kk * 16);
   };
 
@@ -512,7 +542,7 @@ __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
     }
     // software pipeline: the A fragments and B fragments of slice kk+1 are
     // read and dequantized while the 16 products of slice kk run
-    bf16x8 fa[2][8], fb[2][NJ];
+    bf16x8 fa[2][IM], fb[2][NJ];
     read_a(buf, 0, fa[0]);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) fb[0][j] = make_b(wr[PAR], j, 0, T);
@@ -525,7 +555,7 @@ __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
         for (int j = 0; j < NJ; ++j) fb[(kk + 1) & 1][j] = make_b(wr[PAR], j, kk + 1, T);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < IM; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][i], fb[kk & 1][j], acc[i][j], 0, 0, 0);
@@ -534,10 +564,10 @@ __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
         load_x(kn2);
         load_w(kn1, wr[PAR ^ 1]);
       }
-      // 8 NJ x {1 product, a few vector ops, a fragment read, an LDS write,
+      // IM NJ x {1 product, a few vector ops, a fragment read, an LDS write,
       // a memory read}: the vector work runs while the products execute
 #pragma unroll
-      for (int t = 0; t < 8 * NJ; ++t) {
+      for (int t = 0; t < IM * NJ; ++t) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
@@ -596,10 +626,10 @@ __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
   // LDS byte address of this lane's first write: row 4 * (lane >> 5), column lane & 31
   const uint32_t slab_w = (uint32_t)reinterpret_cast<uintptr_t>(slab) +
                           (uint32_t)((4 * (ln >> 5) * SL + (ln & 31)) * 4);
-  const int gc = n0 + wv * 32 * NJ + cc;
-  static_assert(4 * 32 * SL * 4 <= 2 * BM * LDA * 2, "slabs fit in the X buffers");
+  const int gc = n0 + wn * 32 * NJ + cc;
+  static_assert(4 * WM * 32 * SL * 4 <= 2 * BM * LDA * 2, "slabs fit in the X buffers");
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < IM; ++i) {
     // ds_write with the accumulator register as data operand: a plain store
     // makes the compiler copy acc to vector registers first, and that copy
     // pushes the allocator into spilling inside the K loop
@@ -619,7 +649,7 @@ __global__ __launch_bounds__(NT) void prefill_w_kernel(PrefillArgs a) {
 #pragma unroll
     for (int pass = 0; pass < 32 / RP; ++pass) {
       const int rr = pass * RP + rr0;
-      const int gm = m0 + i * 32 + rr;
+      const int gm = m0 + wm * (BM / WM) + i * 32 + rr;
       float v[CW];
 #pragma unroll
       for (int q = 0; q < CW; q += 4) {
@@ -663,9 +693,13 @@ qw_status launch_w(const PrefillArgs &a, int n_begin, int n_tiles, hipStream_t s
   PrefillArgs b = a;
   b.n_begin = n_begin;
   const size_t lds = (size_t)2 * BM * LDA * 2 + (FMT == QW_FMT_NF4_B64 ? 256 * 8 : 0);
-  QW_HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_w_kernel<FMT, F32, NJ>),
+  // one wave per SIMD owning all 256 rows (WM = 1): measured on MI355X, two
+  // waves per SIMD with 128 rows each (WM = 2) are slower, since the two
+  // waves sharing a column both dequantize it
+  constexpr int WM = 1;
+  QW_HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(&prefill_w_kernel<FMT, F32, NJ, WM>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
-  QW_HIP_TRY(launch(prefill_w_kernel<FMT, F32, NJ>, a.mt_count * n_tiles, NT, lds, s, b));
+  QW_HIP_TRY(launch(prefill_w_kernel<FMT, F32, NJ, WM>, a.mt_count * n_tiles, 256 * WM, lds, s, b));
   return QW_OK;
 }
 
@@ -756,6 +790,8 @@ extern "C" qw_status qgemm_prefill(const qw_weight *w, const void *X, int M, voi
   a.n_out = w->format == QW_FMT_2BIT_G32 ? w->n_out : 0;
   a.n_out_pad = w->n_out_pad;
   a.mt_count = (M + BM - 1) / BM;
+  const char *gv = getenv("QW_PREFILL_XCD_GROUP");
+  a.xcd_group = gv ? atoi(gv) : 4;
   const float *L = nf4_levels_host();
   for (int i = 0; i < 16; ++i) a.nf4[i] = L[i];
   const bool f32 = y_dtype == QW_DT_F32;
