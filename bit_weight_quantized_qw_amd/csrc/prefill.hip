@@ -55,8 +55,13 @@ __device__ inline uint32_t f32_to_bf16_bits(float v) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// RNE of both values, one v_cvt_pk_bf16_f32 (converting each half on its own
+// costs two conversions plus a shift and an or)
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 // 32 codes of one group (two code dwords c0, c1 = elements 0..15, 16..31)
