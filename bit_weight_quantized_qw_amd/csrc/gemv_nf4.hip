@@ -13,10 +13,11 @@
 // descriptor) except in the last round, which only drains the ring.
 //
 // Decode: each code byte (two elements) indexes a 256-entry LDS table whose
-// entry holds the pair (L[lo], L[hi]) split into an fp16 high part and an
-// fp16 remainder (L = hi + lo to within 2^-22 relative), so one ds_read_b64
-// feeds two v_dot2_f32_f16 for two weights with exact products and fp32
-// accumulation.
+// entry holds the pair (L[lo], L[hi]) as fp32, so one ds_read_b64 feeds two
+// fp32 FMAs against x (converted to fp32 once): exact x, levels to 2^-24,
+// fp32 products and accumulation. (Two v_dot2_f32_f16 against an fp16
+// high/remainder split of the levels give the same precision but issue at
+// about two thirds of the FMA rate.)
 #include <stdlib.h>
 
 #include "qw_internal.h"
@@ -26,15 +27,13 @@ namespace {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
-struct Nf4Split { uint16_t hi[16], lo[16]; };
-
 struct ArgsNf4 {
   const uint32_t *codes;  // [N][K/8]
   const float *absmax;    // [N][K/64]
   const uint16_t *x;      // [B][K]
   void *y;                // [B][N]
   int N, K, rows_per_wg, W, f32out;
-  Nf4Split L;
+  float L[16];             // NF4 levels
 };
 
 __device__ inline float dot2(uint32_t a, uint32_t b, float c) {
@@ -72,11 +71,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kXLoads = 16;
 constexpr int kThreads = 512;
 
-// LDS: table uint2 [256] | x uint32 [B][K/2] | parts float [rows_per_wg][W][B]
+// LDS: table float2 [256] | x uint32 [B][K/2] | parts float [rows_per_wg][W][B]
 template <int B, int UW, int P>
 __global__ __launch_bounds__(kThreads) void gemv_nf4_kernel(ArgsNf4 a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-  uint2 *table = reinterpret_cast<uint2 *>(lds);
+  float2 *table = reinterpret_cast<float2 *>(lds);
   uint32_t *xl = lds + 512;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
@@ -144,18 +143,13 @@ __global__ __launch_bounds__(kThreads) void gemv_nf4_kernel(ArgsNf4 a) {
   // queued behind the weight prefetch)
   for (int v = threadIdx.x; v < 256; v += kThreads) {
     const int q0 = v & 15, q1 = v >> 4;
-    uint32_t h0 = a.L.hi[0], l0 = a.L.lo[0], h1 = a.L.hi[0], l1 = a.L.lo[0];
+    float l0 = a.L[0], l1 = a.L[0];
 #pragma unroll
     for (int t = 1; t < 16; ++t) {
-      h0 = q0 == t ? a.L.hi[t] : h0;
-      l0 = q0 == t ? a.L.lo[t] : l0;
-      h1 = q1 == t ? a.L.hi[t] : h1;
-      l1 = q1 == t ? a.L.lo[t] : l1;
+      l0 = q0 == t ? a.L[t] : l0;
+      l1 = q1 == t ? a.L[t] : l1;
     }
-    uint2 e;
-    e.x = h0 | (h1 << 16);
-    e.y = l0 | (l1 << 16);
-    table[v] = e;
+    table[v] = make_float2(l0, l1);
   }
 #pragma unroll
   for (int q = 0; q < kXLoads; ++q) {
@@ -167,8 +161,8 @@ __global__ __launch_bounds__(kThreads) void gemv_nf4_kernel(ArgsNf4 a) {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
-  // x pairs of this lane's half blocks (zeros past the row end)
-  u32x4 xr[UW][B][4];
+  // x of this lane's half blocks as fp32 (zeros past the row end)
+  float xf[UW][B][32];
 #pragma unroll
   for (int j = 0; j < UW; ++j) {
     const int h = (j * W + w) * 64 + lane;
@@ -178,43 +172,49 @@ __global__ __launch_bounds__(kThreads) void gemv_nf4_kernel(ArgsNf4 a) {
       for (int q = 0; q < 4; ++q) {
         u32x4 v = {0u, 0u, 0u, 0u};
         if (h < NH) v = reinterpret_cast<const u32x4 *>(xl + b * KP + h * 16)[q];
-        xr[j][b][q] = v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // the element goes through a scalar first: a bit cast of a vector
+          // element reads element 0 with this compiler
+          const uint32_t w32 = v[e];
+          const h2 pr = __builtin_bit_cast(h2, w32);
+          xf[j][b][8 * q + 2 * e] = (float)pr.x;
+          xf[j][b][8 * q + 2 * e + 1] = (float)pr.y;
+        }
       }
   }
 
-  // four independent accumulator chains per part (high, remainder) so the
-  // dot products of one row do not wait on each other
+  // eight independent accumulator chains (code byte position, element
+  // parity) so the FMAs of one row do not wait on each other
   auto compute = [&](const Slot &sl, int rr) __attribute__((always_inline)) {
     float acc[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = 0.0f;
 #pragma unroll
     for (int j = 0; j < UW; ++j) {
-      float th[B][4], tl[B][4];
+      float t[B][8];
 #pragma unroll
       for (int b = 0; b < B; ++b)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) th[b][c] = tl[b][c] = 0.0f;
+        for (int c = 0; c < 8; ++c) t[b][c] = 0.0f;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
         const uint32_t cw = sl.c[j][d];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const uint2 e = table[(cw >> (8 * k)) & 0xFFu];
+          const float2 e = table[(cw >> (8 * k)) & 0xFFu];
 #pragma unroll
           for (int b = 0; b < B; ++b) {
-            const uint32_t xp = xr[j][b][d][k];
-            th[b][k] = dot2(xp, e.x, th[b][k]);
-            tl[b][k] = dot2(xp, e.y, tl[b][k]);
+            t[b][2 * k] = __builtin_fmaf(xf[j][b][8 * d + 2 * k], e.x, t[b][2 * k]);
+            t[b][2 * k + 1] = __builtin_fmaf(xf[j][b][8 * d + 2 * k + 1], e.y, t[b][2 * k + 1]);
           }
         }
       }
       const float am = __builtin_bit_cast(float, sl.am[j]);
 #pragma unroll
       for (int b = 0; b < B; ++b) {
-        const float t = ((th[b][0] + th[b][1]) + (th[b][2] + th[b][3])) +
-                        ((tl[b][0] + tl[b][1]) + (tl[b][2] + tl[b][3]));
-        acc[b] = __builtin_fmaf(am, t, acc[b]);
+        const float s4 = ((t[b][0] + t[b][1]) + (t[b][2] + t[b][3])) + ((t[b][4] + t[b][5]) + (t[b][6] + t[b][7]));
+        acc[b] = __builtin_fmaf(am, s4, acc[b]);
       }
     }
 #pragma unroll
@@ -297,18 +297,6 @@ int env_int(const char *name, int dflt) {
   return v ? atoi(v) : dflt;
 }
 
-Nf4Split split_levels() {
-  Nf4Split sp;
-  const float *L = nf4_levels_host();
-  for (int i = 0; i < 16; ++i) {
-    const uint16_t hb = f64_to_f16_rne((double)L[i]);
-    const double hv = (double)f16_bits_to_f32(hb);
-    sp.hi[i] = hb;
-    sp.lo[i] = f64_to_f16_rne((double)L[i] - hv);
-  }
-  return sp;
-}
-
 }  // namespace
 }  // namespace qw
 
@@ -328,7 +316,6 @@ extern "C" qw_status qgemv_nf4(const qw_weight *w, const void *x, int B, void *y
   const size_t esz = f32 ? 4 : 2;
   const int K = w->K;
   const int NH = K / 32;  // half blocks per row
-  static const Nf4Split sp = split_levels();
   if ((size_t)w->N * (K / 2) >= (1ull << 31)) return QW_ERR_UNSUPPORTED;
   int b0 = 0;
   while (b0 < B) {
@@ -364,7 +351,8 @@ extern "C" qw_status qgemv_nf4(const qw_weight *w, const void *x, int B, void *y
     a.rows_per_wg = rpg;
     a.W = W;
     a.f32out = f32 ? 1 : 0;
-    a.L = sp;
+    const float *lv = nf4_levels_host();
+    for (int i = 0; i < 16; ++i) a.L[i] = lv[i];
     // 3 row slots per wave: measured on MI355X, 6 slots (all rows of a wave
     // in flight at once) are slower with weights coming from HBM;
     // QW_GEMV_NF4_DEEP=1 selects them (tests check both give the same bits)
