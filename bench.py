@@ -57,6 +57,9 @@ class Workload:
     """launches(i): list of (kernel_name, callable) making up step i."""
     name = ""
     library = True  # every launch is one libqw entry-point call
+    # whole-step time from replays of one step captured in a HIP graph (the
+    # per-launch kernel times still come from the eager pass)
+    graph = False
     unit = "GB/s"
     bound = "hbm"
     dtype = "f16"
@@ -236,8 +239,12 @@ class Decode14b(Workload):
 
 
 class Decode32bStack(Workload):
-    """64 layers x {qkv (grouped), o, gate+up (grouped), down}, batch 1."""
+    """64 layers x {qkv (grouped), o, gate+up (grouped), down}, batch 1.
+    One token is 256 launches against distinct per-layer weights; the
+    whole-step time comes from replaying it as a HIP graph, as a decode
+    loop would."""
     name = "decode32b_stack"
+    graph = True
     L, H, I, KV = 64, 5120, 27648, 1024
     PROJ = [("q", 5120, 5120, 0), ("k", 1024, 5120, 0), ("v", 1024, 5120, 0),
             ("o", 5120, 5120, 1), ("gate", 27648, 5120, 2), ("up", 27648, 5120, 2),
@@ -525,7 +532,38 @@ def run(wl, steps, warmup):
     per_kernel = {}
     for name, s_ev, e_ev, _, _ in pairs:
         per_kernel.setdefault(name, []).append(s_ev.elapsed_time(e_ev))
-    return total_ms, per_kernel, (t_wall1 - t_wall0) * 1e3
+    wall_ms = (t_wall1 - t_wall0) * 1e3
+    if wl.graph:
+        total_ms, wall_ms = run_graph(wl, steps)
+    return total_ms, per_kernel, wall_ms
+
+
+def run_graph(wl, steps):
+    """Whole-step time from K replays of step 0 captured in a HIP graph
+    (torch.cuda.CUDAGraph on ROCm); returns (ms of the K replays, wall ms)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _, f in wl.launches(0):  # warm the captured sequence once eagerly
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _, f in wl.launches(0):
+            f()
+    g.replay()
+    torch.cuda.synchronize()
+    first = torch.cuda.Event(enable_timing=True)
+    last = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    first.record()
+    for _ in range(steps):
+        g.replay()
+    last.record()
+    torch.cuda.synchronize()
+    return first.elapsed_time(last), (time.perf_counter() - t0) * 1e3
 
 
 def main():
@@ -579,6 +617,8 @@ def main():
         "kernels": kstats,
         "wall_ms_timed_region": round(wall_ms, 3),
     }
+    if wl.graph:
+        out["step_timing"] = "hip graph replay of one captured step"
     if wl.name == "decode32b_stack":
         out["tokens_per_s"] = round(1e3 / ms_per_step, 2)
     if not args.no_cpu_baseline:
