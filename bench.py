@@ -16,17 +16,22 @@ synthetic input for the chosen workload:
   prefill70b_nf4 / prefill70b_2bit -- 2048x8192 bf16 times 28672x8192;
   copy_calib              -- a plain device copy of 1 GiB (counter scale).
 
-Timing: after W untimed steps, the stream is pre-loaded with a GPU sleep,
-then exactly K steps are enqueued back to back between two HIP events;
-synchronize on both sides. value = algorithmic bytes (GEMV) or flops
-(GEMM) of K steps / time between those two events. Each GEMV weight set
-is rotated over copies totalling >= 1 GiB so HBM, not the 256 MB
-last-level cache, serves it. Every launch in the timed region also carries
-a pair of HIP events that the library attaches to its own kernel dispatch
-(qw_time_next_call), so the pair brackets the kernel's execution alone;
-roofline.achieved = the dominant kernel's algorithmic amount per launch /
-its average duration from those pairs (the figure a kernel trace reports). cpu_baseline times the fp64 oracle on the
-host (product path from packed arrays) on a bounded sample.
+Timing: after W untimed steps, two timed passes over exactly K steps, each
+bracketed by HIP events with synchronization on both sides.
+  - Kernel pass: the K steps are enqueued eagerly behind a GPU sleep; every
+    launch carries a pair of HIP events that the library attaches to its own
+    kernel dispatch (qw_time_next_call), so the pair brackets the kernel's
+    execution alone. roofline.achieved = the dominant kernel's algorithmic
+    amount per launch / its average duration from those pairs (the figure a
+    kernel trace reports).
+  - Step pass: C consecutive steps (the largest divisor of K within 2048
+    launches) are captured in a HIP graph and replayed K / C times, as a
+    decode loop would issue them. value = algorithmic bytes (GEMV) or flops
+    (GEMM) of K steps / time between the events around the replays.
+Each GEMV weight set is rotated over copies totalling >= 1 GiB so HBM, not
+the 256 MB last-level cache, serves it (the captured steps carry their own
+copies). cpu_baseline times the fp64 oracle on the host (product path from
+packed arrays) on a bounded sample.
 """
 
 import argparse
@@ -57,9 +62,9 @@ class Workload:
     """launches(i): list of (kernel_name, callable) making up step i."""
     name = ""
     library = True  # every launch is one libqw entry-point call
-    # whole-step time from replays of one step captured in a HIP graph (the
+    # whole-step time from replays of steps captured in a HIP graph (the
     # per-launch kernel times still come from the eager pass)
-    graph = False
+    graph = True
     unit = "GB/s"
     bound = "hbm"
     dtype = "f16"
@@ -240,11 +245,8 @@ class Decode14b(Workload):
 
 class Decode32bStack(Workload):
     """64 layers x {qkv (grouped), o, gate+up (grouped), down}, batch 1.
-    One token is 256 launches against distinct per-layer weights; the
-    whole-step time comes from replaying it as a HIP graph, as a decode
-    loop would."""
+    One token is 256 launches against distinct per-layer weights."""
     name = "decode32b_stack"
-    graph = True
     L, H, I, KV = 64, 5120, 27648, 1024
     PROJ = [("q", 5120, 5120, 0), ("k", 1024, 5120, 0), ("v", 1024, 5120, 0),
             ("o", 5120, 5120, 1), ("gate", 27648, 5120, 2), ("up", 27648, 5120, 2),
@@ -394,6 +396,7 @@ class Prefill70b(Workload):
 class CopyCalib(Workload):
     name = "copy_calib"
     library = False  # a torch kernel: timed with events recorded around it
+    graph = False
 
     def __init__(self):
         import torch
@@ -538,20 +541,26 @@ def run(wl, steps, warmup):
     return total_ms, per_kernel, wall_ms
 
 
-def run_graph(wl, steps):
-    """Whole-step time from K replays of step 0 captured in a HIP graph
-    (torch.cuda.CUDAGraph on ROCm); returns (ms of the K replays, wall ms)."""
+def run_graph(wl, steps, max_nodes=2048):
+    """Whole-step time of exactly K steps as HIP graph replays
+    (torch.cuda.CUDAGraph on ROCm): C consecutive steps (the largest divisor
+    of K whose launches stay within max_nodes) are captured once, with their
+    own weight copies, and replayed K / C times, as a decode loop would run
+    them. Returns (ms of the K steps, wall ms)."""
     import torch
-    g = torch.cuda.CUDAGraph()
+    lps = max(1, len(wl.launches(0)))
+    c = max(d for d in range(1, steps + 1) if steps % d == 0 and (d * lps <= max_nodes or d == 1))
+    seq = [f for i in range(c) for _, f in wl.launches(i)]
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        for _, f in wl.launches(0):  # warm the captured sequence once eagerly
+        for f in seq:  # warm the captured sequence once eagerly
             f()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for _, f in wl.launches(0):
+        for f in seq:
             f()
     g.replay()
     torch.cuda.synchronize()
@@ -559,7 +568,7 @@ def run_graph(wl, steps):
     last = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     first.record()
-    for _ in range(steps):
+    for _ in range(steps // c):
         g.replay()
     last.record()
     torch.cuda.synchronize()
@@ -618,7 +627,7 @@ def main():
         "wall_ms_timed_region": round(wall_ms, 3),
     }
     if wl.graph:
-        out["step_timing"] = "hip graph replay of one captured step"
+        out["step_timing"] = "hip graph replays of captured steps (kernel times: eager pass)"
     if wl.name == "decode32b_stack":
         out["tokens_per_s"] = round(1e3 / ms_per_step, 2)
     if not args.no_cpu_baseline:
