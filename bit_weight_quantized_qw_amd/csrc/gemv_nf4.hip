@@ -12,12 +12,16 @@
 // every refill is unconditional (rows past the end read through a zero-size
 // descriptor) except in the last round, which only drains the ring.
 //
-// Decode: each code byte (two elements) indexes a 256-entry LDS table whose
-// entry holds the pair (L[lo], L[hi]) as fp32, so one ds_read_b64 feeds two
-// fp32 FMAs against x (converted to fp32 once): exact x, levels to 2^-24,
-// fp32 products and accumulation. (Two v_dot2_f32_f16 against an fp16
-// high/remainder split of the levels give the same precision but issue at
-// about two thirds of the FMA rate.)
+// Decode: each code byte (two elements) selects an LDS entry holding the
+// level pair (L[lo], L[hi]) as fp32, so one ds_read_b64 feeds two fp32 FMAs
+// against x (converted to fp32 once): exact x, levels to 2^-24, fp32
+// products and accumulation. Random byte indices into one 256-entry table
+// would collide in the 32 LDS banks (about 3.5 distinct entries per bank
+// pair and access); instead every entry is stored 16 times, replica r in
+// bank pair r, at byte offset 256*v + 8*r, and lane l reads replica l % 16.
+// The lanes of a 16-lane group then always touch distinct banks, whatever
+// the codes. One v_perm builds the address: the code byte goes to byte 1
+// and the lane's replica offset to byte 0.
 #include <stdlib.h>
 
 #include "qw_internal.h"
@@ -71,12 +75,21 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kXLoads = 16;
 constexpr int kThreads = 512;
 
-// LDS: table float2 [256] | x uint32 [B][K/2] | parts float [rows_per_wg][W][B]
+// Replicated level-pair table: entry v (code byte) replica r at byte
+// 256*v + 8*r, r < 16; bytes 128..255 of each entry are unused.
+constexpr int kPairStride = 256;
+constexpr int kReplicas = 16;
+
+__device__ inline float2 pair_at(const char *tab, uint32_t byte_off) {
+  return *reinterpret_cast<const float2 *>(tab + byte_off);
+}
+
+// LDS: pair table (static, 64 KB) | x uint32 [B][K/2] | parts float [rows_per_wg][W][B]
 template <int B, int UW, int P>
 __global__ __launch_bounds__(kThreads) void gemv_nf4_kernel(ArgsNf4 a) {
+  __shared__ __attribute__((aligned(16))) char pair_tab[256 * kPairStride];
   extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-  float2 *table = reinterpret_cast<float2 *>(lds);
-  uint32_t *xl = lds + 512;
+  uint32_t *xl = lds;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
   const int W = a.W;
@@ -89,9 +102,13 @@ __global__ __launch_bounds__(kThreads) void gemv_nf4_kernel(ArgsNf4 a) {
   float *parts = reinterpret_cast<float *>(xl + B * KP);
   const int g0 = (int)blockIdx.x * a.rows_per_wg;
   const int g1 = min(a.N, g0 + a.rows_per_wg);
-  const int rpw = (a.rows_per_wg + V - 1) / V;
-  const int r0 = min(g1, g0 + (wave / W) * rpw);
-  const int r1 = min(g1, r0 + rpw);
+  // the group's rows split over its V workers as evenly as possible, the
+  // extra rows to the lowest workers: waves v and v + 4 share a SIMD, so no
+  // SIMD gets more than one row above another
+  const int nrow = max(0, g1 - g0), vw = wave / W;
+  const int rbase = nrow / V, rextra = nrow % V;
+  const int r0 = g0 + vw * rbase + min(vw, rextra);
+  const int r1 = r0 + rbase + (vw < rextra ? 1 : 0);
 
   const uint32_t row_cb = (uint32_t)K / 2, row_ab = (uint32_t)NB * 4;  // bytes per row
   uint32_t vc[UW], va[UW];
@@ -137,20 +154,31 @@ __global__ __launch_bounds__(kThreads) void gemv_nf4_kernel(ArgsNf4 a) {
   for (int i = 0; i < P; ++i) issue(ring[i], r0 + i);
   __builtin_amdgcn_sched_barrier(0);
 
-  // level-pair table
-  // (levels picked by a select chain over scalar kernel arguments: a
+  // level-pair table: 16-byte chunk c = 512*i + tid holds two replicas of
+  // entry v = c / 8 (8 used chunks per entry), i.e. low nibble (tid / 8) % 16
+  // and high nibble 4*i + tid / 128, the latter wave-uniform.
+  // (levels picked by select chains over scalar kernel arguments: a
   // per-lane indexed read of the argument block would be a memory load
   // queued behind the weight prefetch)
-  for (int v = threadIdx.x; v < 256; v += kThreads) {
-    const int q0 = v & 15, q1 = v >> 4;
-    float l0 = a.L[0], l1 = a.L[0];
+  {
+    const int qlo = (int)(threadIdx.x >> 3) & 15;
+    float llo = a.L[0];
 #pragma unroll
-    for (int t = 1; t < 16; ++t) {
-      l0 = q0 == t ? a.L[t] : l0;
-      l1 = q1 == t ? a.L[t] : l1;
+    for (int t = 1; t < 16; ++t) llo = qlo == t ? a.L[t] : llo;
+    const int hq = wave >> 1;  // threadIdx.x / 128
+    const int sub = (int)(threadIdx.x & 7);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int qhi = 4 * i + hq;
+      float lhi = a.L[0];
+#pragma unroll
+      for (int t = 1; t < 16; ++t) lhi = qhi == t ? a.L[t] : lhi;
+      const int v = 64 * i + (int)(threadIdx.x >> 3);
+      const float4 two = make_float4(llo, lhi, llo, lhi);
+      *reinterpret_cast<float4 *>(pair_tab + v * kPairStride + sub * 16) = two;
     }
-    table[v] = make_float2(l0, l1);
   }
+  const uint32_t lane_rep = 8u * (uint32_t)(lane % kReplicas);
 #pragma unroll
   for (int q = 0; q < kXLoads; ++q) {
     const int i = q * kThreads + (int)threadIdx.x;
@@ -202,7 +230,9 @@ __global__ __launch_bounds__(kThreads) void gemv_nf4_kernel(ArgsNf4 a) {
         const uint32_t cw = sl.c[j][d];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const float2 e = table[(cw >> (8 * k)) & 0xFFu];
+          // v_perm selector: byte 0 <- lane_rep (source byte 4), byte 1 <-
+          // code byte k, bytes 2..3 <- zero
+          const float2 e = pair_at(pair_tab, __builtin_amdgcn_perm(lane_rep, cw, 0x0C0C0004u | ((uint32_t)k << 8)));
 #pragma unroll
           for (int b = 0; b < B; ++b) {
             t[b][2 * k] = __builtin_fmaf(xf[j][b][8 * d + 2 * k], e.x, t[b][2 * k]);
@@ -321,7 +351,7 @@ extern "C" qw_status qgemv_nf4(const qw_weight *w, const void *x, int B, void *y
   while (b0 < B) {
     const int rest = B - b0;
     int Bk = rest >= 4 ? 4 : (rest >= 2 ? 2 : 1);
-    int W = 0, UW = 0, rpg = 0, grid = 0, rpw = 0;
+    int W = 0, UW = 0, rpg = 0, grid = 0;
     size_t lds = 0;
     for (;;) {
       // half blocks per lane: 4 at batch 1, 2 at batch 2, else 1 (x pairs and
@@ -330,14 +360,12 @@ extern "C" qw_status qgemv_nf4(const qw_weight *w, const void *x, int B, void *y
       W = 1;
       while (W < 8 && W * 64 * maxuw < NH) W *= 2;
       UW = (NH + 64 * W - 1) / (64 * W);
-      const int V = 8 / W;
       const long target_wgs = max(1L, (long)cus * env_int("QW_GEMV_WG_PER_CU", 1));
       rpg = env_int("QW_GEMV_ROWS_PER_WG", 0);
       if (rpg <= 0) rpg = (int)max(1L, ((long)w->N + target_wgs - 1) / target_wgs);
       grid = (w->N + rpg - 1) / rpg;
-      rpw = (rpg + V - 1) / V;
-      lds = 256 * 8 + (size_t)Bk * K * 2 + (W > 1 ? 4 * (size_t)rpg * W * Bk : 0);
-      if (UW <= maxuw && lds <= 160 * 1024 && (Bk * (K / 8) + kThreads - 1) / kThreads <= kXLoads) break;
+      lds = (size_t)Bk * K * 2 + (W > 1 ? 4 * (size_t)rpg * W * Bk : 0);
+      if (UW <= maxuw && lds + 256 * kPairStride <= 160 * 1024 && (Bk * (K / 8) + kThreads - 1) / kThreads <= kXLoads) break;
       if (Bk == 1) return QW_ERR_UNSUPPORTED;
       Bk >>= 1;
     }

@@ -127,10 +127,10 @@ def test_gemv_nf4_llama7b_mlp_shape(B):
     x = inputs.act_f16(B, 4096, workload=2)
     q, a = oracle.quantize_nf4(W)
     ref = oracle.gemv_nf4_ref(x, q, a)
-    y16 = _run_nf4(W, x)
-    e = norm_err(y16, ref)
-    print(f"NF4 11008x4096 B={B} err {e:.3e}")
-    assert e <= TOL
+    e = norm_err(_run_nf4(W, x, f32=True), ref)
+    e16 = norm_err(_run_nf4(W, x), ref)
+    print(f"NF4 11008x4096 B={B} err {e:.3e} (fp16 out {e16:.3e})")
+    assert e <= TOL and e16 <= TOL
 
 
 def test_gemv_2bit_llama7b_mlp_shape():
@@ -150,6 +150,31 @@ def test_gemv_nf4_ragged(N, K, B):
     q, a = oracle.quantize_nf4(W)
     e = norm_err(_run_nf4(W, x, f32=True), oracle.gemv_nf4_ref(x, q, a))
     assert e <= TOL, e
+
+
+@pytest.mark.parametrize("scale", [1e-4, 1.0, 300.0, 60000.0])
+def test_gemv_nf4_input_scales(scale):
+    """fp16 activations from subnormal to near-overflow magnitudes."""
+    W = inputs.weight(256, 1024, workload=77)
+    x = (inputs.act_f16(2, 1024, workload=77).astype(np.float32) * scale)
+    x = np.clip(x, -65504, 65504).astype(np.float16)
+    q, a = oracle.quantize_nf4(W)
+    e = norm_err(_run_nf4(W, x, f32=True), oracle.gemv_nf4_ref(x, q, a))
+    print(f"NF4 input scale {scale}: err {e:.3e}")
+    assert e <= TOL
+
+
+def test_gemv_nf4_one_hot_reads_columns():
+    """x = e_k gives fl32(absmax * L[q]) of column k: one product, one rounding."""
+    W = inputs.weight(200, 512, workload=78)
+    q, a = oracle.quantize_nf4(W)
+    x = np.zeros((2, 512), np.float16)
+    x[0, 7] = 1.0
+    x[1, 300] = 1.0
+    y = _run_nf4(W, x, f32=True)
+    L = oracle.nf4_levels().astype(np.float64)
+    np.testing.assert_array_equal(y[0], (a[:, 7 // 64].astype(np.float64) * L[q[:, 7]]).astype(np.float32))
+    np.testing.assert_array_equal(y[1], (a[:, 300 // 64].astype(np.float64) * L[q[:, 300]]).astype(np.float32))
 
 
 def test_gemv_nf4_fp16_out_is_rounded_fp32_out():
@@ -229,12 +254,11 @@ def test_gemv_nf4_ring_depth_same_bits(N, K, B, monkeypatch):
     W = inputs.weight(N, K, workload=82)
     x = inputs.act_f16(B, K, workload=82)
     q, a = oracle.quantize_nf4(W)
-    ref = oracle.gemv_nf4_ref(x, q, a)
     monkeypatch.setenv("QW_GEMV_NF4_DEEP", "0")
     y3 = _run_nf4(W, x, f32=True)
     monkeypatch.setenv("QW_GEMV_NF4_DEEP", "1")
     y6 = _run_nf4(W, x, f32=True)
-    e = norm_err(y3, ref)
+    e = norm_err(y3, oracle.gemv_nf4_ref(x, q, a))
     print(f"NF4 {N}x{K} B={B}: err {e:.3e} max |diff| {np.abs(y3 - y6).max():.3e}")
     assert e <= TOL
     np.testing.assert_array_equal(y3, y6)
