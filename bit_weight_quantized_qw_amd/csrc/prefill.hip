@@ -401,9 +401,13 @@ template <int FMT, bool F32OUT, int NJ, int WM>
 __global__ __launch_bounds__(256 * WM) void prefill_w_kernel(PrefillArgs a) {
   constexpr int NTW = 256 * WM;  // threads: WM x 4 waves
   constexpr int IM = 8 / WM;     // 32-row blocks per wave
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  // X [BM][LDA] x 2 buffers, then the NF4 table
-  float2 *ltab = reinterpret_cast<float2 *>(smem + 2 * BM * LDA);    // NF4 [256]
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];  // X [BM][LDA] x 2 buffers
+  // NF4 level pairs (L[lo], L[hi]) of each code byte v, 16 replicas: replica r
+  // of entry v at byte 256 v + 8 r, in bank pair r. Lane l reads replica
+  // l % 16, so the table reads of 16 lanes never share a bank whatever the
+  // codes (one 256-entry copy would collide about 3.5 ways per access).
+  __shared__ __attribute__((aligned(16))) char pair_tab[FMT == QW_FMT_NF4_B64 ? 256 * 256 : 16];
+  const uint32_t lane_rep = 8u * (uint32_t)(threadIdx.x & 15);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -417,7 +421,12 @@ __global__ __launch_bounds__(256 * WM) void prefill_w_kernel(PrefillArgs a) {
   const int hk = lane >> 5;  // which 8 of each 16-wide k slice this lane holds
 
   if (FMT == QW_FMT_NF4_B64) {
-    for (int v = tid; v < 256; v += NTW) ltab[v] = make_float2(a.nf4[v & 15], a.nf4[v >> 4]);
+    // 16-byte chunk c holds two replicas of entry c / 8
+    for (int c = tid; c < 256 * 8; c += NTW) {
+      const int v = c >> 3;
+      const float2 p = make_float2(a.nf4[v & 15], a.nf4[v >> 4]);
+      *reinterpret_cast<float4 *>(pair_tab + v * 256 + (c & 7) * 16) = make_float4(p.x, p.y, p.x, p.y);
+    }
   }
 
   // ---- X prefetch registers (IM x 16 bytes per thread per step) ----
@@ -515,7 +524,9 @@ __global__ __launch_bounds__(256 * WM) void prefill_w_kernel(PrefillArgs a) {
       const uint32_t c = hk ? w[j][2 * kk + 1] : w[j][2 * kk];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float2 l = ltab[(c >> (8 * q)) & 0xFFu];
+        // v_perm: byte 0 <- lane_rep (source byte 4), byte 1 <- code byte q
+        const uint32_t ad = __builtin_amdgcn_perm(lane_rep, c, 0x0C0C0004u | ((uint32_t)q << 8));
+        const float2 l = *reinterpret_cast<const float2 *>(pair_tab + ad);
         o[q] = pack_bf16x2(am * l.x, am * l.y);
       }
     }
@@ -697,7 +708,7 @@ qw_status launch_w(const PrefillArgs &a, int n_begin, int n_tiles, hipStream_t s
   if (n_tiles <= 0) return QW_OK;
   PrefillArgs b = a;
   b.n_begin = n_begin;
-  const size_t lds = (size_t)2 * BM * LDA * 2 + (FMT == QW_FMT_NF4_B64 ? 256 * 8 : 0);
+  const size_t lds = (size_t)2 * BM * LDA * 2;  // the NF4 pair table is static
   // one wave per SIMD owning all 256 rows (WM = 1): measured on MI355X, two
   // waves per SIMD with 128 rows each (WM = 2) are slower, since the two
   // waves sharing a column both dequantize it
