@@ -30,7 +30,7 @@ except the two marked "parity unpinned" below:
 
 from .codebook import CODEBOOK_F32, CODEBOOK, lloyd_max_gaussian, gaussian_msqe
 from .rounding import fp16_rne, f32_to_bf16_rne_bits, bf16_bits_to_f64
-from .quant2bit import (GROUP_2BIT, OLS_EPS, assign_codes_2bit, fit_2bit_groups, quantize_2bit,
+from .quant2bit import (GROUP_2BIT, OLS_EPS, assign_codes_2bit, fit_2bit_groups, reassign_nearest_2bit, quantize_2bit,
                         pack_2bit, unpack_2bit, dequant_2bit, sz_interleaved)
 from .nf4 import (BLOCK_NF4, nf4_levels, quantize_nf4, pack_nf4, unpack_nf4,
                   dequant_nf4)
@@ -42,7 +42,7 @@ from .products import (gemv_2bit_ref, gemv_nf4_ref, prefill_weight_bf16_2bit,
 __all__ = [
     "CODEBOOK_F32", "CODEBOOK", "lloyd_max_gaussian", "gaussian_msqe",
     "fp16_rne", "f32_to_bf16_rne_bits", "bf16_bits_to_f64",
-    "GROUP_2BIT", "OLS_EPS", "assign_codes_2bit", "fit_2bit_groups", "quantize_2bit", "pack_2bit", "sz_interleaved",
+    "GROUP_2BIT", "OLS_EPS", "assign_codes_2bit", "fit_2bit_groups", "reassign_nearest_2bit", "quantize_2bit", "pack_2bit", "sz_interleaved",
     "unpack_2bit", "dequant_2bit",
     "BLOCK_NF4", "nf4_levels", "quantize_nf4", "pack_nf4", "unpack_nf4",
     "dequant_nf4",

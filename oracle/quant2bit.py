@@ -30,6 +30,19 @@ design notes):
 * outlier columns are zeroed before quantizing (the full-K layout is kept,
   their codes are stored but never used) and their fp32 weights are kept as
   fp16 anchors.
+
+Optional refinement (a variant of the same format, off by default): the
+section-3 fit takes the codes as given, and section 2 picks each code as the
+nearest centroid. Alternating the two on the fitted levels lowers the
+group's squared error further, as in Lloyd's method. One round:
+* levels l_j = S * C[j] + Z from the unrounded fit (fp64, product then sum);
+* each weight moves to the level nearest to it, |w - l_j| in fp64; a weight
+  whose current level is among the nearest keeps its code, otherwise the
+  lowest nearest j is taken;
+* the fit is redone with the new codes exactly as above (same mean m and
+  deviations d, same sums, same epsilon).
+A round that changes no code leaves S and Z unchanged, so every later round
+does too. S and Z of the last fit are rounded to fp16.
 """
 
 import numpy as np
@@ -60,12 +73,8 @@ def assign_codes_2bit(d, var):
     return q.astype(np.uint8)
 
 
-def fit_2bit_groups(g):
-    """Codes and unrounded fp64 (S, Z) for fp64 groups ``g`` (..., 32)."""
-    m = _seq_sum(g) / GROUP_2BIT
-    d = g - m[..., None]
-    var = _seq_sum(d * d) / GROUP_2BIT
-    q = assign_codes_2bit(d, var)
+def _ols(d, m, q):
+    """Section-3 fit for codes ``q`` given deviations ``d`` = w - m."""
     c = CODEBOOK[q]
     cbar = _seq_sum(c) / GROUP_2BIT
     cc = c - cbar[..., None]
@@ -73,11 +82,38 @@ def fit_2bit_groups(g):
     den = _seq_sum(cc * cc) + OLS_EPS
     S = num / den
     Z = m - S * cbar
+    return S, Z
+
+
+def reassign_nearest_2bit(g, q, S, Z):
+    """Codes of the levels S*C[j] + Z nearest to each weight of ``g`` (..., 32);
+    ties keep the current code ``q`` when it is among the nearest, else take
+    the lowest j."""
+    lev = S[..., None] * CODEBOOK + Z[..., None]              # (..., 4)
+    dist = np.abs(g[..., :, None] - lev[..., None, :])         # (..., 32, 4)
+    best = dist.min(axis=-1)
+    cur = np.take_along_axis(dist, q[..., None].astype(np.int64), axis=-1)[..., 0]
+    first = np.argmax(dist == best[..., None], axis=-1)
+    return np.where(cur == best, q, first).astype(np.uint8)
+
+
+def fit_2bit_groups(g, refine_rounds=0):
+    """Codes and unrounded fp64 (S, Z) for fp64 groups ``g`` (..., 32), after
+    ``refine_rounds`` rounds of reassignment and refit."""
+    m = _seq_sum(g) / GROUP_2BIT
+    d = g - m[..., None]
+    var = _seq_sum(d * d) / GROUP_2BIT
+    q = assign_codes_2bit(d, var)
+    S, Z = _ols(d, m, q)
+    for _ in range(int(refine_rounds)):
+        q = reassign_nearest_2bit(g, q, S, Z)
+        S, Z = _ols(d, m, q)
     return q, S, Z
 
 
-def quantize_2bit(W, outlier_idx=None):
-    """Quantize fp32 ``W`` (N, K) to the 2-bit group code.
+def quantize_2bit(W, outlier_idx=None, refine_rounds=0):
+    """Quantize fp32 ``W`` (N, K) to the 2-bit group code (``refine_rounds``
+    rounds of reassignment and refit after the single pass).
 
     Returns a dict with
       q   : uint8 (N, K) codes 0..3 (unpacked),
@@ -95,7 +131,7 @@ def quantize_2bit(W, outlier_idx=None):
     if idx.size:
         W64[:, idx] = 0.0
 
-    q, S, Z = fit_2bit_groups(W64.reshape(N, K // GROUP_2BIT, GROUP_2BIT))
+    q, S, Z = fit_2bit_groups(W64.reshape(N, K // GROUP_2BIT, GROUP_2BIT), refine_rounds)
     return {
         "q": q.reshape(N, K),
         "S": fp16_rne(S),
@@ -143,5 +179,6 @@ def sz_interleaved(S, Z):
 
 
 __all__ = ["GROUP_2BIT", "OLS_EPS", "CODEBOOK_F32", "assign_codes_2bit", "fit_2bit_groups",
+           "reassign_nearest_2bit",
            "quantize_2bit", "pack_2bit", "unpack_2bit", "dequant_2bit",
            "sz_interleaved"]
