@@ -8,7 +8,15 @@
 // One thread per group (2-bit: 32 weights) or block (NF4: 64 weights); all
 // arithmetic in fp64 with fused multiply-add disabled and every sum taken
 // left to right, so the packed result is bit-identical to a plain
-// sequential fp64 evaluation of the same formulas.
+// sequential fp64 evaluation of the same formulas. Weights may be fp32,
+// fp16 or bf16; each widens exactly to fp32 before anything else.
+//
+// Optional refinement of the 2-bit code (0 rounds by default): section 3
+// fits S, Z to given codes and section 2 assigns each weight its nearest
+// centroid; a round applies that rule to the fitted levels S*C[j] + Z (a
+// weight keeps its code when that level is among the nearest, else takes the
+// lowest nearest j) and refits, as in Lloyd's method. Each round can only
+// lower the group's squared error (up to the epsilon of the fit).
 #include <math.h>
 
 #include "qw_internal.h"
@@ -18,15 +26,29 @@ namespace {
 
 struct Levels16 { float v[16]; };
 
+// Exact widening of one stored weight to fp32.
+struct Bf16 { uint16_t bits; };
+__device__ inline float widen(float v) { return v; }
+__device__ inline float widen(_Float16 v) { return (float)v; }
+__device__ inline float widen(Bf16 v) { return __builtin_bit_cast(float, (uint32_t)v.bits << 16); }
+
+template <typename WT>
+__device__ inline void load_row_run(const WT *__restrict__ p, float *out, int count) {
+#pragma unroll
+  for (int i = 0; i < count; ++i) out[i] = widen(p[i]);
+}
+
+template <typename WT>
 __global__ __launch_bounds__(256) void pack2_kernel(
-    const float *__restrict__ W, int N, int K, const int32_t *__restrict__ idx,
-    int n_out, uint32_t *__restrict__ codes, uint32_t *__restrict__ sz) {
+    const WT *__restrict__ W, int N, int K, const int32_t *__restrict__ idx,
+    int n_out, int rounds, uint32_t *__restrict__ codes, uint32_t *__restrict__ sz) {
 #pragma clang fp contract(off)
   const int G = K / 32;
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (long)N * G) return;
   const int n = (int)(gid / G), g = (int)(gid % G);
-  const float4 *wp = reinterpret_cast<const float4 *>(W + (size_t)n * K + (size_t)g * 32);
+  float wf[32];
+  load_row_run(W + (size_t)n * K + (size_t)g * 32, wf, 32);
 
   // positions of this group that are anchor channels
   uint32_t omask = 0;
@@ -42,13 +64,7 @@ __global__ __launch_bounds__(256) void pack2_kernel(
 
   double w[32];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float4 v = wp[i];
-    w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
-  }
-#pragma unroll
-  for (int i = 0; i < 32; ++i)
-    if ((omask >> i) & 1u) w[i] = 0.0;
+  for (int i = 0; i < 32; ++i) w[i] = ((omask >> i) & 1u) ? 0.0 : (double)wf[i];
 
   double acc = 0.0;
 #pragma unroll
@@ -67,28 +83,50 @@ __global__ __launch_bounds__(256) void pack2_kernel(
   const double thr = (t * t) * var;
 
   uint32_t q[32];
-  double c[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
     const bool outer = (d[i] * d[i]) > thr;
     const bool upper = d[i] >= 0.0;
     q[i] = upper ? (outer ? 3u : 2u) : (outer ? 0u : 1u);
-    c[i] = upper ? (outer ? C3 : C2) : (outer ? C0 : C1);
   }
-  acc = 0.0;
+  const double Cv[4] = {C0, C1, C2, C3};
+  // section-3 fit of the current codes
+  double S, Z;
+  auto fit = [&]() __attribute__((always_inline)) {
+    double c[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) acc = acc + c[i];
-  const double cbar = acc / 32.0;
-  double num = 0.0, den = 0.0;
+    for (int i = 0; i < 32; ++i) c[i] = q[i] == 0 ? C0 : (q[i] == 1 ? C1 : (q[i] == 2 ? C2 : C3));
+    double a = 0.0;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const double cc = c[i] - cbar;
-    num = num + d[i] * cc;
-    den = den + cc * cc;
+    for (int i = 0; i < 32; ++i) a = a + c[i];
+    const double cbar = a / 32.0;
+    double num = 0.0, den = 0.0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const double cc = c[i] - cbar;
+      num = num + d[i] * cc;
+      den = den + cc * cc;
+    }
+    den = den + 1e-8;
+    S = num / den;
+    Z = m - S * cbar;
+  };
+  fit();
+  for (int r = 0; r < rounds; ++r) {
+    double lev[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lev[j] = S * Cv[j] + Z;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      double dist[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dist[j] = fabs(w[i] - lev[j]);
+      const double best = fmin(fmin(dist[0], dist[1]), fmin(dist[2], dist[3]));
+      const double cur = q[i] == 0 ? dist[0] : (q[i] == 1 ? dist[1] : (q[i] == 2 ? dist[2] : dist[3]));
+      if (!(cur == best)) q[i] = dist[0] == best ? 0u : (dist[1] == best ? 1u : (dist[2] == best ? 2u : 3u));
+    }
+    fit();
   }
-  den = den + 1e-8;
-  const double S = num / den;
-  const double Z = m - S * cbar;
 
   uint32_t lo32 = 0, hi32 = 0;
 #pragma unroll
@@ -103,8 +141,9 @@ __global__ __launch_bounds__(256) void pack2_kernel(
   sz[(size_t)n * G + g] = (uint32_t)f64_to_f16_rne(S) | ((uint32_t)f64_to_f16_rne(Z) << 16);
 }
 
+template <typename WT>
 __global__ __launch_bounds__(256) void anchors_kernel(
-    const float *__restrict__ W, int N, int K, const int32_t *__restrict__ idx,
+    const WT *__restrict__ W, int N, int K, const int32_t *__restrict__ idx,
     int n_out, int n_out_pad, uint16_t *__restrict__ out_w) {
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (long)N * n_out_pad) return;
@@ -112,7 +151,7 @@ __global__ __launch_bounds__(256) void anchors_kernel(
   uint16_t v = 0;
   if (o < n_out) {
     const int c = idx[o];
-    if (c >= 0 && c < K) v = f64_to_f16_rne((double)W[(size_t)n * K + c]);
+    if (c >= 0 && c < K) v = f64_to_f16_rne((double)widen(W[(size_t)n * K + c]));
   }
   out_w[gid] = v;
 }
@@ -136,21 +175,17 @@ __global__ __launch_bounds__(256) void mask_kernel(const int32_t *__restrict__ i
   mask[i] = m;
 }
 
+template <typename WT>
 __global__ __launch_bounds__(256) void pack_nf4_kernel(
-    const float *__restrict__ W, int N, int K, Levels16 L,
+    const WT *__restrict__ W, int N, int K, Levels16 L,
     uint32_t *__restrict__ codes, float *__restrict__ absmax) {
 #pragma clang fp contract(off)
   const int G = K / 64;
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (long)N * G) return;
   const int n = (int)(gid / G), g = (int)(gid % G);
-  const float4 *wp = reinterpret_cast<const float4 *>(W + (size_t)n * K + (size_t)g * 64);
   float w[64];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float4 v = wp[i];
-    w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
-  }
+  load_row_run(W + (size_t)n * K + (size_t)g * 64, w, 64);
   float a = 0.0f;
 #pragma unroll
   for (int i = 0; i < 64; ++i) a = fmaxf(a, fabsf(w[i]));
@@ -181,27 +216,61 @@ __global__ __launch_bounds__(256) void pack_nf4_kernel(
 
 // --- outlier selection ------------------------------------------------------
 
+// Column statistic of W for the score: mean |W[:, c]| or ||W[:, c]||_2,
+// fp64, rows summed in order.
+template <typename WT>
+__device__ inline double column_stat(const WT *__restrict__ W, int N, int K, int c, int kind) {
+#pragma clang fp contract(off)
+  double acc = 0.0;
+  if (kind == QW_SCORE_MEANABS) {
+    for (int n = 0; n < N; ++n) acc = acc + fabs((double)widen(W[(size_t)n * K + c]));
+    acc = acc / (double)N;
+  } else {
+    for (int n = 0; n < N; ++n) {
+      const double v = (double)widen(W[(size_t)n * K + c]);
+      acc = acc + v * v;
+    }
+    acc = sqrt(acc);
+  }
+  return acc;
+}
+
 __global__ __launch_bounds__(256) void score_kernel(
     const float *__restrict__ W, int N, int K, const float *__restrict__ X,
     int P, int kind, double *__restrict__ score) {
 #pragma clang fp contract(off)
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= K) return;
-  double acc = 0.0;
-  if (kind == QW_SCORE_MEANABS) {
-    for (int n = 0; n < N; ++n) acc = acc + fabs((double)W[(size_t)n * K + c]);
-    acc = acc / (double)N;
-  } else {
-    for (int n = 0; n < N; ++n) {
-      const double v = (double)W[(size_t)n * K + c];
-      acc = acc + v * v;
-    }
-    acc = sqrt(acc);
-  }
+  const double acc = column_stat(W, N, K, c, kind);
   double pm = 0.0;
   for (int p = 0; p < P; ++p) pm = pm + fabs((double)X[(size_t)p * K + c]);
   pm = pm / (double)P;
   score[c] = acc * pm;
+}
+
+// Score from accumulated profile sums: the same value as score_kernel gives
+// for the profile rows those sums ran over, in the same order.
+template <typename WT>
+__global__ __launch_bounds__(256) void score_prof_kernel(
+    const WT *__restrict__ W, int N, int K, const double *__restrict__ abs_sum,
+    double rows, int kind, double *__restrict__ score) {
+#pragma clang fp contract(off)
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= K) return;
+  score[c] = column_stat(W, N, K, c, kind) * (abs_sum[c] / rows);
+}
+
+// abs_sum[c] += |X[0][c]| + |X[1][c]| + ... (fp64, in row order): one thread
+// per channel, so a wave reads 64 consecutive channels of a row.
+template <typename XT>
+__global__ __launch_bounds__(256) void profile_kernel(const XT *__restrict__ X, int M, int K,
+                                                      double *__restrict__ abs_sum) {
+#pragma clang fp contract(off)
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= K) return;
+  double acc = abs_sum[c];
+  for (int m = 0; m < M; ++m) acc = acc + fabs((double)widen(X[(size_t)m * K + c]));
+  abs_sum[c] = acc;
 }
 
 // flag[c] = 1 when fewer than n channels beat c (higher score, or equal
@@ -251,31 +320,18 @@ __global__ __launch_bounds__(1024) void compact_kernel(const int32_t *__restrict
 
 unsigned grid_for(long work, int block) { return (unsigned)((work + block - 1) / block); }
 
-}  // namespace
-}  // namespace qw
-
-extern "C" {
-
-qw_status qw_pack(const float *W, const qw_weight *dst, void *stream) {
-  using namespace qw;
-  CallScope scope;
-  if (!W || !dst) return QW_ERR_INVALID_ARG;
-  qw_status st = check_weight_view(dst, dst->format, 0);
-  if (st != QW_OK) return st;
-  if (!aligned16(W)) return QW_ERR_ALIGNMENT;
+template <typename WT>
+qw_status pack_typed(const WT *W, int rounds, const qw_weight *dst, hipStream_t s) {
   const int N = dst->N, K = dst->K, n_out = dst->n_out;
-  st = current_device(nullptr);
-  if (st != QW_OK) return st;
-  hipStream_t s = as_stream(stream);
   if (dst->format == QW_FMT_2BIT_G32) {
     const long groups = (long)N * (K / 32);
-    QW_HIP_TRY(launch(pack2_kernel, grid_for(groups, 256), 256, 0, s, W, N, K,
-                      (const int32_t *)dst->out_idx, n_out,
+    QW_HIP_TRY(launch(pack2_kernel<WT>, grid_for(groups, 256), 256, 0, s, W, N, K,
+                      (const int32_t *)dst->out_idx, n_out, rounds,
                       reinterpret_cast<uint32_t *>(dst->codes),
                       reinterpret_cast<uint32_t *>(dst->scales)));
     if (n_out > 0) {
       const long cnt = (long)N * dst->n_out_pad;
-      QW_HIP_TRY(launch(anchors_kernel, grid_for(cnt, 256), 256, 0, s, W, N, K,
+      QW_HIP_TRY(launch(anchors_kernel<WT>, grid_for(cnt, 256), 256, 0, s, W, N, K,
                         (const int32_t *)dst->out_idx, n_out, (int)dst->n_out_pad,
                         dst->out_w));
       QW_HIP_TRY(launch(mask_kernel, grid_for(K / 32, 256), 256, 0, s,
@@ -286,9 +342,71 @@ qw_status qw_pack(const float *W, const qw_weight *dst, void *stream) {
     const float *h = nf4_levels_host();
     for (int i = 0; i < 16; ++i) L.v[i] = h[i];
     const long blocks = (long)N * (K / 64);
-    QW_HIP_TRY(launch(pack_nf4_kernel, grid_for(blocks, 256), 256, 0, s, W, N, K, L,
+    QW_HIP_TRY(launch(pack_nf4_kernel<WT>, grid_for(blocks, 256), 256, 0, s, W, N, K, L,
                       reinterpret_cast<uint32_t *>(dst->codes),
                       reinterpret_cast<float *>(dst->scales)));
+  }
+  return QW_OK;
+}
+
+// Top-n channels of a score vector in device scratch -> out_idx (ascending).
+qw_status rank_and_compact(const double *sc, int32_t *flag, int K, int n, int32_t *out_idx,
+                           hipStream_t s) {
+  QW_HIP_TRY(launch(rank_kernel, grid_for(K, 256), 256, 0, s, sc, K, n, flag));
+  QW_HIP_TRY(launch(compact_kernel, 1, 1024, 0, s, (const int32_t *)flag, K, n, out_idx));
+  return QW_OK;
+}
+
+}  // namespace
+}  // namespace qw
+
+extern "C" {
+
+qw_status qw_pack(const float *W, const qw_weight *dst, void *stream) {
+  return qw_pack_ex(W, QW_DT_F32, 0, dst, stream);
+}
+
+qw_status qw_pack_ex(const void *W, qw_dtype w_dtype, int refine_rounds, const qw_weight *dst,
+                     void *stream) {
+  using namespace qw;
+  CallScope scope;
+  if (!W || !dst) return QW_ERR_INVALID_ARG;
+  if (w_dtype != QW_DT_F32 && w_dtype != QW_DT_F16 && w_dtype != QW_DT_BF16) return QW_ERR_INVALID_ARG;
+  qw_status st = check_weight_view(dst, dst->format, 0);
+  if (st != QW_OK) return st;
+  if (refine_rounds < 0 || refine_rounds > QW_MAX_REFINE_ROUNDS) return QW_ERR_INVALID_ARG;
+  if (dst->format != QW_FMT_2BIT_G32 && refine_rounds != 0) return QW_ERR_INVALID_ARG;
+  if (!aligned16(W)) return QW_ERR_ALIGNMENT;
+  st = current_device(nullptr);
+  if (st != QW_OK) return st;
+  hipStream_t s = as_stream(stream);
+  switch (w_dtype) {
+    case QW_DT_F16: return pack_typed(reinterpret_cast<const _Float16 *>(W), refine_rounds, dst, s);
+    case QW_DT_BF16: return pack_typed(reinterpret_cast<const Bf16 *>(W), refine_rounds, dst, s);
+    default: return pack_typed(reinterpret_cast<const float *>(W), refine_rounds, dst, s);
+  }
+}
+
+qw_status qw_profile_accumulate(const void *X, qw_dtype x_dtype, int M, int K, double *abs_sum,
+                                void *stream) {
+  using namespace qw;
+  CallScope scope;
+  if (!X || !abs_sum || M <= 0 || K <= 0) return QW_ERR_INVALID_ARG;
+  if (x_dtype != QW_DT_F32 && x_dtype != QW_DT_F16 && x_dtype != QW_DT_BF16) return QW_ERR_INVALID_ARG;
+  if (!aligned16(X) || !aligned16(abs_sum)) return QW_ERR_ALIGNMENT;
+  qw_status st = current_device(nullptr);
+  if (st != QW_OK) return st;
+  hipStream_t s = as_stream(stream);
+  const unsigned grid = grid_for(K, 256);
+  switch (x_dtype) {
+    case QW_DT_F16:
+      QW_HIP_TRY(launch(profile_kernel<_Float16>, grid, 256, 0, s, reinterpret_cast<const _Float16 *>(X), M, K, abs_sum));
+      break;
+    case QW_DT_BF16:
+      QW_HIP_TRY(launch(profile_kernel<Bf16>, grid, 256, 0, s, reinterpret_cast<const Bf16 *>(X), M, K, abs_sum));
+      break;
+    default:
+      QW_HIP_TRY(launch(profile_kernel<float>, grid, 256, 0, s, reinterpret_cast<const float *>(X), M, K, abs_sum));
   }
   return QW_OK;
 }
@@ -320,6 +438,49 @@ qw_status qw_select_outliers(const float *W, int N, int K, const float *X_prof, 
     e = launch(compact_kernel, 1, 1024, 0, s, (const int32_t *)flag, K, n, out_idx);
   hipError_t fe = hipFreeAsync(scratch, s);
   if (e != hipSuccess || fe != hipSuccess) return QW_ERR_HIP;
+  return QW_OK;
+}
+
+qw_status qw_select_outliers_ex(const void *W, qw_dtype w_dtype, int N, int K,
+                                const double *prof_abs_sum, long long prof_rows, double frac,
+                                qw_score score, int32_t *out_idx, void *stream) {
+  using namespace qw;
+  CallScope scope;
+  if (!W || !prof_abs_sum || N <= 0 || K <= 0 || prof_rows <= 0) return QW_ERR_INVALID_ARG;
+  if (w_dtype != QW_DT_F32 && w_dtype != QW_DT_F16 && w_dtype != QW_DT_BF16) return QW_ERR_INVALID_ARG;
+  if (score != QW_SCORE_MEANABS && score != QW_SCORE_L2) return QW_ERR_INVALID_ARG;
+  const int n = qw_outlier_count(K, frac);
+  if (n < 0) return QW_ERR_INVALID_ARG;
+  if (n > 0 && !out_idx) return QW_ERR_INVALID_ARG;
+  if (!aligned16(W) || !aligned16(prof_abs_sum) || (n > 0 && !aligned16(out_idx))) return QW_ERR_ALIGNMENT;
+  qw_status st = current_device(nullptr);
+  if (st != QW_OK) return st;
+  if (n == 0) return QW_OK;
+  hipStream_t s = as_stream(stream);
+  void *scratch = nullptr;
+  const size_t bytes = (size_t)K * (sizeof(double) + sizeof(int32_t));
+  QW_HIP_TRY(hipMallocAsync(&scratch, bytes, s));
+  double *sc = reinterpret_cast<double *>(scratch);
+  int32_t *flag = reinterpret_cast<int32_t *>(sc + K);
+  const unsigned grid = grid_for(K, 256);
+  const double rows = (double)prof_rows;
+  hipError_t e;
+  switch (w_dtype) {
+    case QW_DT_F16:
+      e = launch(score_prof_kernel<_Float16>, grid, 256, 0, s, reinterpret_cast<const _Float16 *>(W), N, K,
+                 prof_abs_sum, rows, (int)score, sc);
+      break;
+    case QW_DT_BF16:
+      e = launch(score_prof_kernel<Bf16>, grid, 256, 0, s, reinterpret_cast<const Bf16 *>(W), N, K,
+                 prof_abs_sum, rows, (int)score, sc);
+      break;
+    default:
+      e = launch(score_prof_kernel<float>, grid, 256, 0, s, reinterpret_cast<const float *>(W), N, K,
+                 prof_abs_sum, rows, (int)score, sc);
+  }
+  qw_status rs = e == hipSuccess ? rank_and_compact(sc, flag, K, n, out_idx, s) : QW_ERR_HIP;
+  hipError_t fe = hipFreeAsync(scratch, s);
+  if (rs != QW_OK || fe != hipSuccess) return QW_ERR_HIP;
   return QW_OK;
 }
 

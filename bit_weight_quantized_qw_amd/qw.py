@@ -26,6 +26,7 @@ QW_SCORE_MEANABS, QW_SCORE_L2 = 1, 2
 EXPORTS = [
     "qw_abi_version", "qw_status_str", "qw_time_next_call", "qw_packed_sizes", "qw_outlier_count",
     "qw_codebook_2bit", "qw_nf4_levels", "qw_select_outliers", "qw_pack",
+    "qw_pack_ex", "qw_profile_accumulate", "qw_select_outliers_ex",
     "qgemv_2bit", "qgemv_nf4", "qgemv_2bit_grouped", "qgemm_prefill",
 ]
 
@@ -77,6 +78,9 @@ def lib():
         "qw_nf4_levels": (c_i, [ctypes.POINTER(ctypes.c_float)]),
         "qw_select_outliers": (c_i, [c_p, c_i, c_i, c_p, c_i, c_d, c_i, c_p, c_p]),
         "qw_pack": (c_i, [c_p, W, c_p]),
+        "qw_pack_ex": (c_i, [c_p, c_i, c_i, W, c_p]),
+        "qw_profile_accumulate": (c_i, [c_p, c_i, c_i, c_i, c_p, c_p]),
+        "qw_select_outliers_ex": (c_i, [c_p, c_i, c_i, c_i, c_p, ctypes.c_longlong, c_d, c_i, c_p, c_p]),
         "qgemv_2bit": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
         "qgemv_nf4": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
         "qgemv_2bit_grouped": (c_i, [W, c_i, c_p, c_i, ctypes.POINTER(c_p), c_i, c_p]),
@@ -224,10 +228,37 @@ def qw_select_outliers(W, X_prof, frac, score=QW_SCORE_MEANABS):
     return out[:n]
 
 
+def _w_dtype(t):
+    import torch
+    m = {torch.float32: QW_DT_F32, torch.float16: QW_DT_F16, torch.bfloat16: QW_DT_BF16}
+    if t.dtype not in m:
+        raise TypeError(f"weights/activations must be fp32, fp16 or bf16, got {t.dtype}")
+    return m[t.dtype]
+
+
+def _need_any(t, name, ndim):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+    return _w_dtype(t)
+
+
 def qw_pack(W, fmt=QW_FMT_2BIT_G32, out_idx=None):
     """Quantize and pack fp32 W (N, K) on the device; returns PackedWeight."""
     import torch
     _need(W, torch.float32, "W", 2)
+    return qw_pack_ex(W, fmt, out_idx)
+
+
+def qw_pack_ex(W, fmt=QW_FMT_2BIT_G32, out_idx=None, refine_rounds=0):
+    """qw_pack for fp32, fp16 or bf16 W (N, K), with ``refine_rounds`` rounds
+    of nearest-level reassignment and refit (2-bit); returns PackedWeight."""
+    import torch
+    dt = _need_any(W, "W", 2)
     N, K = W.shape
     n_out = 0 if out_idx is None else int(out_idx.numel())
     pw = PackedWeight(fmt, N, K, n_out, device=W.device)
@@ -238,8 +269,37 @@ def qw_pack(W, fmt=QW_FMT_2BIT_G32, out_idx=None):
             raise ValueError("out_idx must be strictly ascending channels in [0, K)")
         pw.out_idx.copy_(out_idx)
     v = pw.view()
-    _check(lib().qw_pack(_ptr(W), ctypes.byref(v), _stream()), "qw_pack")
+    _check(lib().qw_pack_ex(_ptr(W), dt, int(refine_rounds), ctypes.byref(v), _stream()), "qw_pack_ex")
     return pw
+
+
+def qw_profile_accumulate(X, abs_sum):
+    """abs_sum (float64 [K], device) += column sums of |X| (M, K) in row order."""
+    import torch
+    dt = _need_any(X, "X", 2)
+    _need(abs_sum, torch.float64, "abs_sum", 1)
+    M, K = X.shape
+    if abs_sum.numel() != K:
+        raise ValueError("abs_sum must have K entries")
+    _check(lib().qw_profile_accumulate(_ptr(X), dt, M, K, _ptr(abs_sum), _stream()),
+           "qw_profile_accumulate")
+    return abs_sum
+
+
+def qw_select_outliers_ex(W, prof_abs_sum, prof_rows, frac, score=QW_SCORE_MEANABS):
+    """Anchor channels from accumulated profile sums (qw_profile_accumulate)."""
+    import torch
+    dt = _need_any(W, "W", 2)
+    _need(prof_abs_sum, torch.float64, "prof_abs_sum", 1)
+    N, K = W.shape
+    n = qw_outlier_count(K, frac)
+    if n < 0:
+        raise ValueError("frac must be in [0, 1)")
+    out = torch.empty(max(n, 1), dtype=torch.int32, device=W.device)
+    _check(lib().qw_select_outliers_ex(_ptr(W), dt, N, K, _ptr(prof_abs_sum), int(prof_rows),
+                                       float(frac), int(score), _ptr(out), _stream()),
+           "qw_select_outliers_ex")
+    return out[:n]
 
 
 _OUT = {"f16": QW_DT_F16, "bf16": QW_DT_BF16, "f32": QW_DT_F32}

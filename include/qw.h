@@ -171,6 +171,61 @@ qw_status qw_select_outliers(const float *W, int N, int K, const float *X_prof,
  * Python binding checks it). */
 qw_status qw_pack(const float *W, const qw_weight *dst, void *stream);
 
+/* Maximum refine_rounds accepted by qw_pack_ex. */
+#define QW_MAX_REFINE_ROUNDS 64
+
+/* qw_pack with a choice of weight storage type and an optional refinement
+ * of the 2-bit code.
+ *   W        device [N][K] in w_dtype: QW_DT_F32, QW_DT_F16 or QW_DT_BF16;
+ *            each weight widens exactly to fp32, so fp16/bf16 weights give
+ *            the same result as their fp32 values passed to qw_pack
+ *            (anchors: fp16 rounding of that value).
+ *   refine_rounds  0..QW_MAX_REFINE_ROUNDS, 2-bit only (0 for NF4):
+ *            after the single pass, rounds of
+ *              (a) levels l_j = S*C[j] + Z of the unrounded fit (fp64,
+ *                  product then sum);
+ *              (b) every weight takes the level nearest to it, |w - l_j| in
+ *                  fp64, keeping its code when that level is among the
+ *                  nearest, else the lowest nearest j;
+ *              (c) the section-3 fit redone for the new codes (same mean,
+ *                  sums and epsilon as the single pass).
+ *            The nearest-centroid rule of section 2 applied to the fitted
+ *            levels, alternated with the fit of section 3 as in Lloyd's
+ *            method; no round raises the group's squared error (beyond the
+ *            epsilon's effect), and S, Z of the last fit are stored.
+ * Buffers and other rules as qw_pack, whose result qw_pack_ex(W, QW_DT_F32,
+ * 0, dst, stream) is. The result is bit-identical to the reference
+ * quantizer run with the same rounds. Errors: INVALID_ARG (dtype, rounds
+ * out of range or non-zero for NF4, and the qw_pack checks), ALIGNMENT,
+ * HIP. */
+qw_status qw_pack_ex(const void *W, qw_dtype w_dtype, int refine_rounds,
+                     const qw_weight *dst, void *stream);
+
+/* Calibration statistic of section 4 ("we record the average activation
+ * magnitude for each column"), accumulated on the device over any number
+ * of batches so the profile never has to be held at once:
+ *   abs_sum[c] += |X[0][c]| + |X[1][c]| + ... + |X[M-1][c]|
+ * in fp64, rows added in order (so batches given in order sum exactly as
+ * one long profile would).
+ *   X        device [M][K] in x_dtype (F32, F16 or BF16), M >= 1
+ *   abs_sum  device double [K], caller-initialised (zeros before the first
+ *            batch); read and written.
+ * Errors: INVALID_ARG, ALIGNMENT, HIP. */
+qw_status qw_profile_accumulate(const void *X, qw_dtype x_dtype, int M, int K,
+                                double *abs_sum, void *stream);
+
+/* qw_select_outliers from accumulated profile sums instead of the profile
+ * rows: the mean magnitude of channel c is prof_abs_sum[c] / prof_rows, and
+ * W may be fp32, fp16 or bf16 (widened exactly). With sums from
+ * qw_profile_accumulate over the same rows, in the same order, the chosen
+ * channels are identical to qw_select_outliers on those rows.
+ *   prof_abs_sum device double [K]; prof_rows >= 1 rows summed.
+ * Scratch and errors as qw_select_outliers. */
+qw_status qw_select_outliers_ex(const void *W, qw_dtype w_dtype, int N, int K,
+                                const double *prof_abs_sum, long long prof_rows,
+                                double frac, qw_score score, int32_t *out_idx,
+                                void *stream);
+
 /* Decode GEMV for the 2-bit format:
  *   y[b][n] = sum_k x_R[b][k] w_hat[n][k] + sum_o x[b][out_idx[o]] out_w[n][o]
  * for b < B, where x_R is x with the anchor channels set to zero.

@@ -34,7 +34,7 @@ from .quant2bit import (GROUP_2BIT, OLS_EPS, assign_codes_2bit, fit_2bit_groups,
                         pack_2bit, unpack_2bit, dequant_2bit, sz_interleaved)
 from .nf4 import (BLOCK_NF4, nf4_levels, quantize_nf4, pack_nf4, unpack_nf4,
                   dequant_nf4)
-from .outliers import (outlier_count, profile_absmean, channel_scores,
+from .outliers import (outlier_count, profile_abs_sum, profile_absmean, channel_scores,
                        select_outliers, SCORE_MEANABS, SCORE_L2)
 from .products import (gemv_2bit_ref, gemv_nf4_ref, prefill_weight_bf16_2bit,
                        prefill_weight_bf16_nf4, gemm_prefill_ref)
@@ -46,7 +46,7 @@ __all__ = [
     "unpack_2bit", "dequant_2bit",
     "BLOCK_NF4", "nf4_levels", "quantize_nf4", "pack_nf4", "unpack_nf4",
     "dequant_nf4",
-    "outlier_count", "profile_absmean", "channel_scores", "select_outliers",
+    "outlier_count", "profile_abs_sum", "profile_absmean", "channel_scores", "select_outliers",
     "SCORE_MEANABS", "SCORE_L2",
     "gemv_2bit_ref", "gemv_nf4_ref", "prefill_weight_bf16_2bit",
     "prefill_weight_bf16_nf4", "gemm_prefill_ref",

@@ -38,10 +38,15 @@ def _seq_row_sum(a):
     return acc
 
 
+def profile_abs_sum(Xp):
+    """Sum over calibration rows of |X[:, c]| (fp64, rows added in order)."""
+    X64 = np.asarray(Xp, dtype=np.float32).astype(np.float64)
+    return _seq_row_sum(np.abs(X64))
+
+
 def profile_absmean(Xp):
     """Mean over calibration rows of |X[:, c]| (fp64, sequential)."""
-    X64 = np.asarray(Xp, dtype=np.float32).astype(np.float64)
-    return _seq_row_sum(np.abs(X64)) / X64.shape[0]
+    return profile_abs_sum(Xp) / np.asarray(Xp).shape[0]
 
 
 def channel_scores(W, Xp, kind=SCORE_MEANABS):

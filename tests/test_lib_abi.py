@@ -116,6 +116,28 @@ def test_validation_before_device_work(L):
     assert L.qw_select_outliers(p, 4, 64, p, 2, 0.1, 7, p, s) == qw.QW_ERR_INVALID_ARG
 
 
+def test_validation_of_pack_ex_and_profile_calls(L):
+    s = ctypes.c_void_p(0)
+    p = ctypes.c_void_p(0x1000)
+    v2 = _view(qw.QW_FMT_2BIT_G32, 16, 64)
+    v4 = _view(qw.QW_FMT_NF4_B64, 16, 64)
+    # bad weight dtype, rounds out of range, rounds for NF4
+    assert L.qw_pack_ex(p, 9, 0, ctypes.byref(v2), s) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_pack_ex(p, qw.QW_DT_F16, -1, ctypes.byref(v2), s) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_pack_ex(p, qw.QW_DT_F16, 65, ctypes.byref(v2), s) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_pack_ex(p, qw.QW_DT_BF16, 1, ctypes.byref(v4), s) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_pack_ex(ctypes.c_void_p(0x1002), qw.QW_DT_F16, 1, ctypes.byref(v2), s) == qw.QW_ERR_ALIGNMENT
+    # profile: sizes, dtype, alignment
+    assert L.qw_profile_accumulate(p, qw.QW_DT_F16, 0, 64, p, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_profile_accumulate(p, 7, 4, 64, p, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_profile_accumulate(p, qw.QW_DT_BF16, 4, 64, None, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_profile_accumulate(p, qw.QW_DT_F32, 4, 64, ctypes.c_void_p(0x1008), s) == qw.QW_ERR_ALIGNMENT
+    # selection from sums: rows, fraction, score kind
+    assert L.qw_select_outliers_ex(p, qw.QW_DT_F16, 4, 64, p, 0, 0.1, 1, p, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_select_outliers_ex(p, qw.QW_DT_F16, 4, 64, p, 8, 1.0, 1, p, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_select_outliers_ex(p, qw.QW_DT_F16, 4, 64, p, 8, 0.1, 3, p, s) == qw.QW_ERR_INVALID_ARG
+
+
 def test_valid_call_without_gpu_reports_no_device(L):
     import torch
     if torch.cuda.is_available():
