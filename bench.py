@@ -14,6 +14,10 @@ synthetic input for the chosen workload:
   decode32b_stack         -- one token through the 448 projection GEMVs of a
       64-layer 32B-shaped decoder (q/k/v and gate/up grouped per launch);
   prefill70b_nf4 / prefill70b_2bit -- 2048x8192 bf16 times 28672x8192;
+  prep_llama7b_refine5    -- preparing the 11008x4096 weight from fp16: device
+      profile sums over 256 calibration rows, 3.5% anchor selection, 2-bit
+      pack with 5 refinement rounds (value: fp16 weight GB/s; the packer is
+      bound by fp64 arithmetic, its roofline is the fp64 vector peak);
   copy_calib              -- a plain device copy of 1 GiB (counter scale).
 
 Timing: after W untimed steps, two timed passes over exactly K steps, each
@@ -49,6 +53,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fused 2-bit dequant-GEMV achieved HBM GB/s and % of peak; prefill GEMM TFLOP/s"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP64_PEAK_TFLOPS = 78.6
 ROTATE_BYTES = 1 << 30
 
 
@@ -393,6 +398,70 @@ class Prefill70b(Workload):
                             f"2048x8192 X times a 512x8192 slice of W (fp64)", scale=1e12)
 
 
+# fp64 operations per group of 32 in the 2-bit packer, counted from its
+# formulas: single pass (mean, deviations, variance, squared deviations, the
+# fit's sums, S and Z) 360; a refinement round (4 levels, 4 distances and 3
+# minimum steps per weight, the refit) 429.
+PACK2_FLOPS_PASS, PACK2_FLOPS_ROUND = 360, 429
+
+
+class PrepLlama7b(Workload):
+    """Device-side weight preparation of one 11008x4096 projection from fp16
+    weights: profile sums, anchor selection, refined 2-bit pack."""
+    name = "prep_llama7b_refine5"
+    N, K, P, ROUNDS = 11008, 4096, 256, 5
+    graph = False  # the selection allocates stream-ordered scratch
+    bound = "alu"
+    dtype = "f64"
+
+    def __init__(self):
+        import torch
+        from bit_weight_quantized_qw_amd import inputs, qw
+        self.qw = qw
+        self.Wh = inputs.weight(self.N, self.K, workload=2).astype(np.float16)
+        self.Xh = inputs.profile(self.P, self.K, workload=2).astype(np.float16)
+        self.W = torch.from_numpy(self.Wh.view(np.int16)).cuda().view(torch.float16)
+        self.X = torch.from_numpy(self.Xh.view(np.int16)).cuda().view(torch.float16)
+        self.acc = torch.zeros(self.K, dtype=torch.float64, device="cuda")
+        self.n_out = qw.qw_outlier_count(self.K, 0.035)
+        self.idx = None
+
+    def _select(self):
+        self.idx = self.qw.qw_select_outliers_ex(self.W, self.acc, self.P, 0.035)
+
+    def launches(self, i):
+        return [("qw_profile_accumulate", lambda: (self.acc.zero_(), self.qw.qw_profile_accumulate(self.X, self.acc))),
+                ("qw_select_outliers_ex", self._select),
+                ("qw_pack_ex", lambda: self.qw.qw_pack_ex(self.W, self.qw.QW_FMT_2BIT_G32, self.idx,
+                                                          refine_rounds=self.ROUNDS))]
+
+    def kernel_amount(self):  # fp16 bytes each call consumes
+        wb = self.N * self.K * 2
+        return {"qw_profile_accumulate": self.P * self.K * 2, "qw_select_outliers_ex": wb, "qw_pack_ex": wb}
+
+    def roof_amount(self):  # fp64 operations of the packer per call
+        groups = self.N * self.K // 32
+        return {"qw_pack_ex": groups * (PACK2_FLOPS_PASS + self.ROUNDS * PACK2_FLOPS_ROUND)}
+
+    def step_amount(self):
+        return self.N * self.K * 2
+
+    def config(self):
+        return {"workload": self.name, "N": self.N, "K": self.K, "weights": "fp16",
+                "profile_rows": self.P, "anchors": self.n_out, "refine_rounds": self.ROUNDS}
+
+    def cpu_baseline(self):
+        import oracle
+        rows = 512
+        W32 = self.Wh[:rows].astype(np.float32)
+        X32 = self.Xh.astype(np.float32)
+
+        def one():
+            idx = oracle.select_outliers(W32, X32, 0.035)
+            oracle.quantize_2bit(W32, idx, refine_rounds=self.ROUNDS)
+        return _time_oracle(one, rows * self.K * 2, f"{rows} of the {self.N} rows (profile, selection, 5-round pack)")
+
+
 class CopyCalib(Workload):
     name = "copy_calib"
     library = False  # a torch kernel: timed with events recorded around it
@@ -460,6 +529,7 @@ WORKLOADS = {
     "decode14b_b4": lambda: Decode14b(4), "decode14b_b8": lambda: Decode14b(8),
     "decode32b_stack": Decode32bStack,
     "prefill70b_nf4": lambda: Prefill70b(2), "prefill70b_2bit": lambda: Prefill70b(1),
+    "prep_llama7b_refine5": PrepLlama7b,
     "copy_calib": CopyCalib,
 }
 
@@ -613,6 +683,11 @@ def main():
     dominant = max(kstats, key=lambda k: kstats[k]["avg_us"] * kstats[k]["launches"])
     peak = BF16_PEAK_TFLOPS if wl.bound == "mfma" else HBM_PEAK_GBS
     ach = kstats[dominant]["achieved"]
+    roof_unit = wl.unit
+    if wl.bound == "alu" and dominant in wl.roof_amount():  # fp64 operations per launch / time
+        peak, roof_unit = FP64_PEAK_TFLOPS, "TFLOP/s"
+        avg_s = kstats[dominant]["avg_us"] * 1e-6
+        ach = round(wl.roof_amount()[dominant] / avg_s / 1e12, 3)
     traffic = _traffic(args.traffic_json, wl.name, dominant)
 
     out = {
@@ -622,7 +697,7 @@ def main():
         "dtype": wl.dtype, "data": "synthetic (seeded N(0,0.02^2) weights, N(0,1) activations)",
         "config": wl.config(),
         "roofline": {"bound": wl.bound, "kernel": dominant, "achieved": ach, "peak": peak,
-                     "unit": wl.unit, "frac": round(ach / peak, 4), "traffic": traffic},
+                     "unit": roof_unit, "frac": round(ach / peak, 4), "traffic": traffic},
         "kernels": kstats,
         "wall_ms_timed_region": round(wall_ms, 3),
     }

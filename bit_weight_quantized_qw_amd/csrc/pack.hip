@@ -216,61 +216,89 @@ __global__ __launch_bounds__(256) void pack_nf4_kernel(
 
 // --- outlier selection ------------------------------------------------------
 
-// Column statistic of W for the score: mean |W[:, c]| or ||W[:, c]||_2,
-// fp64, rows summed in order.
-template <typename WT>
-__device__ inline double column_stat(const WT *__restrict__ W, int N, int K, int c, int kind) {
+// Column sums over rows, in row order, in fp64: out[c] = init[c] + f(A[0][c])
+// + f(A[1][c]) + ... with f = |a| (kind 0) or a*a (kind 1). One workgroup per
+// 64 columns: all four waves load chunks of 128 rows (coalesced across the
+// columns, 32 loads in flight per thread, rows past R as zeros) into LDS
+// while wave 0 adds the previous chunk row by row, one column per lane, so
+// every column's sum is the plain sequential one. init, if given, must be
+// non-negative (it is an earlier sum of this kind).
+constexpr int kColChunk = 128;
+
+// One element through a buffer load: offsets past the descriptor's size
+// read as zero, so guarded loads need no branch and all stay in flight.
+__device__ inline __amdgpu_buffer_rsrc_t elem_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ inline float load_elem(__amdgpu_buffer_rsrc_t r, uint32_t off, const float *) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ inline float load_elem(__amdgpu_buffer_rsrc_t r, uint32_t off, const _Float16 *) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
+}
+__device__ inline float load_elem(__amdgpu_buffer_rsrc_t r, uint32_t off, const Bf16 *) {
+  return __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0) << 16);
+}
+constexpr uint32_t kElemOob = 0x7FFFFFF0u;
+
+template <typename T, int KIND>
+__global__ __launch_bounds__(256) void colsum_kernel(const T *__restrict__ A, int R, int C,
+                                                     const double *__restrict__ init,
+                                                     double *__restrict__ out) {
 #pragma clang fp contract(off)
-  double acc = 0.0;
-  if (kind == QW_SCORE_MEANABS) {
-    for (int n = 0; n < N; ++n) acc = acc + fabs((double)widen(W[(size_t)n * K + c]));
-    acc = acc / (double)N;
-  } else {
-    for (int n = 0; n < N; ++n) {
-      const double v = (double)widen(W[(size_t)n * K + c]);
-      acc = acc + v * v;
+  __shared__ float tile[2][kColChunk][64];
+  const int t = threadIdx.x, lane = t & 63, r_off = t >> 6;
+  const int c = blockIdx.x * 64 + lane;
+  const bool cok = c < C;
+  // the host keeps R * C * sizeof(T) below 2^31
+  const auto rs = elem_rsrc(A, (uint32_t)((size_t)R * C * sizeof(T)));
+  float v[kColChunk / 4];
+  auto load = [&](int r0) {
+#pragma unroll
+    for (int i = 0; i < kColChunk / 4; ++i) {
+      const int r = r0 + r_off + 4 * i;
+      const uint32_t off = (cok && r < R) ? (uint32_t)(((size_t)r * C + c) * sizeof(T)) : kElemOob;
+      v[i] = load_elem(rs, off, A);
     }
-    acc = sqrt(acc);
+  };
+  auto store = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < kColChunk / 4; ++i) tile[b][r_off + 4 * i][lane] = v[i];
+  };
+  double acc = (init && cok) ? init[c] : 0.0;
+  const int nch = (R + kColChunk - 1) / kColChunk;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int ch = 0; ch < nch; ++ch) {
+    const int b = ch & 1;
+    if (ch + 1 < nch) load((ch + 1) * kColChunk);
+    if (t < 64) {
+      // rows past R hold +0: adding +0 to a sum that is never -0 (it starts
+      // at +0 or at an earlier sum of non-negative terms) changes no bit, so
+      // the whole chunk is added without a row test and the reads batch up
+#pragma unroll
+      for (int r = 0; r < kColChunk; ++r) {
+        const double x = (double)tile[b][r][lane];
+        acc = acc + (KIND == 0 ? fabs(x) : x * x);
+      }
+    }
+    if (ch + 1 < nch) store(b ^ 1);
+    __syncthreads();
   }
-  return acc;
+  if (t < 64 && cok) out[c] = acc;
 }
 
-__global__ __launch_bounds__(256) void score_kernel(
-    const float *__restrict__ W, int N, int K, const float *__restrict__ X,
-    int P, int kind, double *__restrict__ score) {
+// score[c] = stat(W column c) * profile mean of channel c, with the column
+// sum of W already in score[c]: MEANABS divides it by N, L2 takes its root.
+__global__ __launch_bounds__(256) void score_finish_kernel(double *__restrict__ score, int K, int N,
+                                                          int kind, const double *__restrict__ prof_sum,
+                                                          double rows) {
 #pragma clang fp contract(off)
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= K) return;
-  const double acc = column_stat(W, N, K, c, kind);
-  double pm = 0.0;
-  for (int p = 0; p < P; ++p) pm = pm + fabs((double)X[(size_t)p * K + c]);
-  pm = pm / (double)P;
-  score[c] = acc * pm;
-}
-
-// Score from accumulated profile sums: the same value as score_kernel gives
-// for the profile rows those sums ran over, in the same order.
-template <typename WT>
-__global__ __launch_bounds__(256) void score_prof_kernel(
-    const WT *__restrict__ W, int N, int K, const double *__restrict__ abs_sum,
-    double rows, int kind, double *__restrict__ score) {
-#pragma clang fp contract(off)
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= K) return;
-  score[c] = column_stat(W, N, K, c, kind) * (abs_sum[c] / rows);
-}
-
-// abs_sum[c] += |X[0][c]| + |X[1][c]| + ... (fp64, in row order): one thread
-// per channel, so a wave reads 64 consecutive channels of a row.
-template <typename XT>
-__global__ __launch_bounds__(256) void profile_kernel(const XT *__restrict__ X, int M, int K,
-                                                      double *__restrict__ abs_sum) {
-#pragma clang fp contract(off)
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= K) return;
-  double acc = abs_sum[c];
-  for (int m = 0; m < M; ++m) acc = acc + fabs((double)widen(X[(size_t)m * K + c]));
-  abs_sum[c] = acc;
+  const double col = kind == QW_SCORE_MEANABS ? score[c] / (double)N : sqrt(score[c]);
+  score[c] = col * (prof_sum[c] / rows);
 }
 
 // flag[c] = 1 when fewer than n channels beat c (higher score, or equal
@@ -393,20 +421,24 @@ qw_status qw_profile_accumulate(const void *X, qw_dtype x_dtype, int M, int K, d
   CallScope scope;
   if (!X || !abs_sum || M <= 0 || K <= 0) return QW_ERR_INVALID_ARG;
   if (x_dtype != QW_DT_F32 && x_dtype != QW_DT_F16 && x_dtype != QW_DT_BF16) return QW_ERR_INVALID_ARG;
+  if ((size_t)M * K * (x_dtype == QW_DT_F32 ? 4 : 2) >= (1ull << 31)) return QW_ERR_UNSUPPORTED;
   if (!aligned16(X) || !aligned16(abs_sum)) return QW_ERR_ALIGNMENT;
   qw_status st = current_device(nullptr);
   if (st != QW_OK) return st;
   hipStream_t s = as_stream(stream);
-  const unsigned grid = grid_for(K, 256);
+  const unsigned grid = grid_for(K, 64);
   switch (x_dtype) {
     case QW_DT_F16:
-      QW_HIP_TRY(launch(profile_kernel<_Float16>, grid, 256, 0, s, reinterpret_cast<const _Float16 *>(X), M, K, abs_sum));
+      QW_HIP_TRY(launch(colsum_kernel<_Float16, 0>, grid, 256, 0, s, reinterpret_cast<const _Float16 *>(X), M, K,
+                        (const double *)abs_sum, abs_sum));
       break;
     case QW_DT_BF16:
-      QW_HIP_TRY(launch(profile_kernel<Bf16>, grid, 256, 0, s, reinterpret_cast<const Bf16 *>(X), M, K, abs_sum));
+      QW_HIP_TRY(launch(colsum_kernel<Bf16, 0>, grid, 256, 0, s, reinterpret_cast<const Bf16 *>(X), M, K,
+                        (const double *)abs_sum, abs_sum));
       break;
     default:
-      QW_HIP_TRY(launch(profile_kernel<float>, grid, 256, 0, s, reinterpret_cast<const float *>(X), M, K, abs_sum));
+      QW_HIP_TRY(launch(colsum_kernel<float, 0>, grid, 256, 0, s, reinterpret_cast<const float *>(X), M, K,
+                        (const double *)abs_sum, abs_sum));
   }
   return QW_OK;
 }
@@ -416,6 +448,7 @@ qw_status qw_select_outliers(const float *W, int N, int K, const float *X_prof, 
   using namespace qw;
   CallScope scope;
   if (!W || !X_prof || N <= 0 || K <= 0 || P <= 0) return QW_ERR_INVALID_ARG;
+  if ((size_t)N * K * 4 >= (1ull << 31) || (size_t)P * K * 4 >= (1ull << 31)) return QW_ERR_UNSUPPORTED;
   if (score != QW_SCORE_MEANABS && score != QW_SCORE_L2) return QW_ERR_INVALID_ARG;
   const int n = qw_outlier_count(K, frac);
   if (n < 0) return QW_ERR_INVALID_ARG;
@@ -426,18 +459,23 @@ qw_status qw_select_outliers(const float *W, int N, int K, const float *X_prof, 
   if (n == 0) return QW_OK;
   hipStream_t s = as_stream(stream);
   void *scratch = nullptr;
-  const size_t bytes = (size_t)K * (sizeof(double) + sizeof(int32_t));
+  const size_t bytes = (size_t)K * (2 * sizeof(double) + sizeof(int32_t));
   QW_HIP_TRY(hipMallocAsync(&scratch, bytes, s));
   double *sc = reinterpret_cast<double *>(scratch);
-  int32_t *flag = reinterpret_cast<int32_t *>(sc + K);
-  hipError_t e = launch(score_kernel, grid_for(K, 256), 256, 0, s, W, N, K, X_prof, P,
-                        (int)score, sc);
+  double *prof = sc + K;
+  int32_t *flag = reinterpret_cast<int32_t *>(prof + K);
+  const unsigned cgrid = grid_for(K, 64);
+  hipError_t e = score == QW_SCORE_MEANABS
+                     ? launch(colsum_kernel<float, 0>, cgrid, 256, 0, s, W, N, K, (const double *)nullptr, sc)
+                     : launch(colsum_kernel<float, 1>, cgrid, 256, 0, s, W, N, K, (const double *)nullptr, sc);
   if (e == hipSuccess)
-    e = launch(rank_kernel, grid_for(K, 256), 256, 0, s, (const double *)sc, K, n, flag);
+    e = launch(colsum_kernel<float, 0>, cgrid, 256, 0, s, X_prof, P, K, (const double *)nullptr, prof);
   if (e == hipSuccess)
-    e = launch(compact_kernel, 1, 1024, 0, s, (const int32_t *)flag, K, n, out_idx);
+    e = launch(score_finish_kernel, grid_for(K, 256), 256, 0, s, sc, K, N, (int)score,
+               (const double *)prof, (double)P);
+  qw_status rs = e == hipSuccess ? rank_and_compact(sc, flag, K, n, out_idx, s) : QW_ERR_HIP;
   hipError_t fe = hipFreeAsync(scratch, s);
-  if (e != hipSuccess || fe != hipSuccess) return QW_ERR_HIP;
+  if (rs != QW_OK || fe != hipSuccess) return QW_ERR_HIP;
   return QW_OK;
 }
 
@@ -448,6 +486,7 @@ qw_status qw_select_outliers_ex(const void *W, qw_dtype w_dtype, int N, int K,
   CallScope scope;
   if (!W || !prof_abs_sum || N <= 0 || K <= 0 || prof_rows <= 0) return QW_ERR_INVALID_ARG;
   if (w_dtype != QW_DT_F32 && w_dtype != QW_DT_F16 && w_dtype != QW_DT_BF16) return QW_ERR_INVALID_ARG;
+  if ((size_t)N * K * (w_dtype == QW_DT_F32 ? 4 : 2) >= (1ull << 31)) return QW_ERR_UNSUPPORTED;
   if (score != QW_SCORE_MEANABS && score != QW_SCORE_L2) return QW_ERR_INVALID_ARG;
   const int n = qw_outlier_count(K, frac);
   if (n < 0) return QW_ERR_INVALID_ARG;
@@ -462,22 +501,31 @@ qw_status qw_select_outliers_ex(const void *W, qw_dtype w_dtype, int N, int K,
   QW_HIP_TRY(hipMallocAsync(&scratch, bytes, s));
   double *sc = reinterpret_cast<double *>(scratch);
   int32_t *flag = reinterpret_cast<int32_t *>(sc + K);
-  const unsigned grid = grid_for(K, 256);
-  const double rows = (double)prof_rows;
+  const unsigned cgrid = grid_for(K, 64);
+  const bool l2 = score == QW_SCORE_L2;
   hipError_t e;
   switch (w_dtype) {
-    case QW_DT_F16:
-      e = launch(score_prof_kernel<_Float16>, grid, 256, 0, s, reinterpret_cast<const _Float16 *>(W), N, K,
-                 prof_abs_sum, rows, (int)score, sc);
+    case QW_DT_F16: {
+      const _Float16 *w = reinterpret_cast<const _Float16 *>(W);
+      e = l2 ? launch(colsum_kernel<_Float16, 1>, cgrid, 256, 0, s, w, N, K, (const double *)nullptr, sc)
+             : launch(colsum_kernel<_Float16, 0>, cgrid, 256, 0, s, w, N, K, (const double *)nullptr, sc);
       break;
-    case QW_DT_BF16:
-      e = launch(score_prof_kernel<Bf16>, grid, 256, 0, s, reinterpret_cast<const Bf16 *>(W), N, K,
-                 prof_abs_sum, rows, (int)score, sc);
+    }
+    case QW_DT_BF16: {
+      const Bf16 *w = reinterpret_cast<const Bf16 *>(W);
+      e = l2 ? launch(colsum_kernel<Bf16, 1>, cgrid, 256, 0, s, w, N, K, (const double *)nullptr, sc)
+             : launch(colsum_kernel<Bf16, 0>, cgrid, 256, 0, s, w, N, K, (const double *)nullptr, sc);
       break;
-    default:
-      e = launch(score_prof_kernel<float>, grid, 256, 0, s, reinterpret_cast<const float *>(W), N, K,
-                 prof_abs_sum, rows, (int)score, sc);
+    }
+    default: {
+      const float *w = reinterpret_cast<const float *>(W);
+      e = l2 ? launch(colsum_kernel<float, 1>, cgrid, 256, 0, s, w, N, K, (const double *)nullptr, sc)
+             : launch(colsum_kernel<float, 0>, cgrid, 256, 0, s, w, N, K, (const double *)nullptr, sc);
+    }
   }
+  if (e == hipSuccess)
+    e = launch(score_finish_kernel, grid_for(K, 256), 256, 0, s, sc, K, N, (int)score, prof_abs_sum,
+               (double)prof_rows);
   qw_status rs = e == hipSuccess ? rank_and_compact(sc, flag, K, n, out_idx, s) : QW_ERR_HIP;
   hipError_t fe = hipFreeAsync(scratch, s);
   if (rs != QW_OK || fe != hipSuccess) return QW_ERR_HIP;

@@ -145,7 +145,7 @@ qw_status qw_nf4_levels(float *out);
  *   out_idx device int32 [n]   receives the n highest-scoring channels in
  *          ascending order; ties in score go to the lower channel.
  * Scores are fp64 with sequential sums over rows. Uses a device scratch
- * buffer of K*12 bytes that it allocates and frees with the stream-ordered
+ * buffer of K*20 bytes that it allocates and frees with the stream-ordered
  * allocator on ``stream``. Errors: INVALID_ARG for bad sizes or NULL
  * pointers, HIP if the allocation or a launch fails. */
 qw_status qw_select_outliers(const float *W, int N, int K, const float *X_prof,
@@ -220,7 +220,8 @@ qw_status qw_profile_accumulate(const void *X, qw_dtype x_dtype, int M, int K,
  * qw_profile_accumulate over the same rows, in the same order, the chosen
  * channels are identical to qw_select_outliers on those rows.
  *   prof_abs_sum device double [K]; prof_rows >= 1 rows summed.
- * Scratch and errors as qw_select_outliers. */
+ * Uses K*12 bytes of stream-ordered scratch (allocated and freed on
+ * ``stream``). Errors as qw_select_outliers. */
 qw_status qw_select_outliers_ex(const void *W, qw_dtype w_dtype, int N, int K,
                                 const double *prof_abs_sum, long long prof_rows,
                                 double frac, qw_score score, int32_t *out_idx,
