@@ -201,9 +201,9 @@ qw_status qw_pack(const float *W, const qw_weight *dst, void *stream);
 qw_status qw_pack_ex(const void *W, qw_dtype w_dtype, int refine_rounds,
                      const qw_weight *dst, void *stream);
 
-/* Calibration statistic of section 4 ("we record the average activation
- * magnitude for each column"), accumulated on the device over any number
- * of batches so the profile never has to be held at once:
+/* Calibration statistic of section 4 (the mean activation magnitude of
+ * each input channel over a calibration pass), accumulated on the device
+ * over any number of batches so the profile never has to be held at once:
  *   abs_sum[c] += |X[0][c]| + |X[1][c]| + ... + |X[M-1][c]|
  * in fp64, rows added in order (so batches given in order sum exactly as
  * one long profile would).
