@@ -13,6 +13,8 @@ synthetic input for the chosen workload:
   decode14b_b{1,2,4,8}    -- 2-bit GEMV 13824x5120 with 179 fp16 anchors;
   decode32b_stack         -- one token through the 448 projection GEMVs of a
       64-layer 32B-shaped decoder (q/k/v and gate/up grouped per launch);
+  decode32b_stack_fused   -- the same token as one persistent launch with a
+      device-wide barrier between its 256 stages;
   prefill70b_nf4 / prefill70b_2bit -- 2048x8192 bf16 times 28672x8192;
   prep_llama7b_refine5    -- preparing the 11008x4096 weight from fp16: device
       profile sums over 256 calibration rows, 3.5% anchor selection, 2-bit
@@ -346,6 +348,45 @@ class Decode32bStack(Workload):
         return _time_oracle(one, amount, "layer 0, first 1/8 of the rows of each of the 7 projections")
 
 
+class Decode32bStackFused(Decode32bStack):
+    """The same token (same weights, inputs and the 448 products) as one
+    persistent launch: the 256 stages run in order with a device-wide barrier
+    between consecutive stages (qw_stack_run)."""
+    name = "decode32b_stack_fused"
+    graph = False  # one launch per token already
+
+    def __init__(self, layers=None):
+        super().__init__(layers)
+        qw = self.qw
+        self.ybuf = {}
+        stages = []
+        for l in range(self.L):
+            d, x = self.w[l], self.xs[l]
+            stages += [
+                ([d["q"], d["k"], d["v"]], x[0][0, :self.H], [self.yq[0], self.yk[0], self.yv[0]]),
+                ([d["o"]], x[1][0, :self.H], [self.yo[0]]),
+                ([d["gate"], d["up"]], x[2][0, :self.H], [self.yg[0], self.yu[0]]),
+                ([d["down"]], x[3][0, :self.I], [self.yd[0]]),
+            ]
+        self.stack = qw.Stack(stages)
+        log(f"stack: {len(stages)} stages planned, {self.stack.handle.lds} B LDS per workgroup")
+
+    def launches(self, i):
+        return [("stack", self.stack.run)]
+
+    def kernel_amount(self):
+        return {"stack": self.L * sum(Decode32bStack.kernel_amount(self).values())}
+
+    def step_amount(self):
+        return self.kernel_amount()["stack"]
+
+    def config(self):
+        c = super().config()
+        c["workload"] = self.name
+        c["launches_per_token"] = 1
+        return c
+
+
 class Prefill70b(Workload):
     M, N, K = 2048, 28672, 8192
     unit = "TFLOP/s"
@@ -528,6 +569,7 @@ WORKLOADS = {
     "decode14b_b1": lambda: Decode14b(1), "decode14b_b2": lambda: Decode14b(2),
     "decode14b_b4": lambda: Decode14b(4), "decode14b_b8": lambda: Decode14b(8),
     "decode32b_stack": Decode32bStack,
+    "decode32b_stack_fused": Decode32bStackFused,
     "prefill70b_nf4": lambda: Prefill70b(2), "prefill70b_2bit": lambda: Prefill70b(1),
     "prep_llama7b_refine5": PrepLlama7b,
     "copy_calib": CopyCalib,
@@ -703,8 +745,10 @@ def main():
     }
     if wl.graph:
         out["step_timing"] = "hip graph replays of captured steps (kernel times: eager pass)"
-    if wl.name == "decode32b_stack":
+    if wl.name.startswith("decode32b_stack"):
         out["tokens_per_s"] = round(1e3 / ms_per_step, 2)
+    if hasattr(wl, "stack"):
+        out["barrier_timeouts"] = wl.stack.error()
     if not args.no_cpu_baseline:
         cb = wl.cpu_baseline()
         if cb is not None:

@@ -133,6 +133,20 @@ hipError_t launch_raw(const void *fn, dim3 grid, dim3 block, void **argv, size_t
   return hipExtLaunchKernel(fn, grid, block, argv, lds, s, start, tl_call_stop, 0);
 }
 
+hipError_t launch_cooperative_raw(const void *fn, dim3 grid, dim3 block, void **argv, size_t lds,
+                                  hipStream_t s) {
+  // a cooperative launch takes no attached events: the call's start (if
+  // still unrecorded) and stop go on the stream around it
+  if (tl_call_start) {
+    const hipError_t e = hipEventRecord(tl_call_start, s);
+    tl_call_start = nullptr;
+    if (e != hipSuccess) return e;
+  }
+  const hipError_t e = hipLaunchCooperativeKernel(fn, grid, block, argv, (unsigned)lds, s);
+  if (e != hipSuccess || !tl_call_stop) return e;
+  return hipEventRecord(tl_call_stop, s);
+}
+
 }  // namespace qw
 
 extern "C" {

@@ -41,6 +41,8 @@
 // and are added in a fixed order.
 #include <stdlib.h>
 
+#include <vector>
+
 #include "qw_internal.h"
 
 namespace qw {
@@ -125,6 +127,14 @@ __device__ inline u32x2 ld2(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
 }
 __device__ inline u32x4 ld4(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)v, (int)s, 0);
+}
+// Cache policy sc0 | sc1 (system coherence): the access goes to memory past
+// the per-CU and per-XCD caches, so data written by workgroups on other XCDs
+// is seen without invalidating any cache, and stores are visible to them as
+// soon as they complete.
+constexpr int kCoherent = 1 | 16;
+__device__ inline u32x4 ld4_coherent(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t s) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)v, (int)s, kCoherent);
 }
 
 __device__ inline v4f mfma_x_codes(v8i a_fp8, v8i b_fp4) {
@@ -214,9 +224,10 @@ __device__ inline T sel4(int i, T v0, T v1, T v2, T v3) {
   return r;
 }
 
-template <int B, int P, bool MULTI>
-__global__ __launch_bounds__(kThreads) void kernel(Args a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+// One workgroup's share (workgroup index bid of the launch the Args were
+// planned for) of a grouped GEMV, with the group's LDS at lds.
+template <int B, int P, bool MULTI, bool XC = false>
+__device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -224,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void kernel(Args a) {
   if (MULTI) {
 #pragma unroll
     for (int i = 1; i < kMats; ++i)
-      if (i < a.count && (int)blockIdx.x >= a.m[i].wg_begin) mi = i;
+      if (i < a.count && bid >= a.m[i].wg_begin) mi = i;
   }
   // each field picked with constant indices (scalar selects, no copy of the
   // argument block into private memory)
@@ -242,7 +253,7 @@ __global__ __launch_bounds__(kThreads) void kernel(Args a) {
   const int K = a.K;
   const int G = K >> 5;
   const int SC = K >> 9;
-  const int wi = (int)blockIdx.x - M.wg_begin;
+  const int wi = bid - M.wg_begin;
   // (wi + 1) * tiles < 2^31: tiles <= 2^27 and workgroups per matrix <= 16
   // per CU of a 256-CU part are checked on the host
   const int t0 = (int)((uint32_t)(wi * M.tiles) / (uint32_t)M.wg_count);
@@ -336,7 +347,8 @@ __global__ __launch_bounds__(kThreads) void kernel(Args a) {
 #pragma unroll
       for (int t = 1; t < B; ++t) b += bg >= t * G;
       const int gr = bg - b * G;
-      xv[q] = ld4(r_x, ok ? (uint32_t)((b * K + gr * 32 + qt * 8) * 2) : kOob, 0);
+      const uint32_t xoff = ok ? (uint32_t)((b * K + gr * 32 + qt * 8) * 2) : kOob;
+      xv[q] = XC ? ld4_coherent(r_x, xoff, 0) : ld4(r_x, xoff, 0);
       if (has_mask) mk[q] = ld1(r_mask, ok ? (uint32_t)gr * 4 : kOob, 0);
     }
   }
@@ -591,11 +603,85 @@ __global__ __launch_bounds__(kThreads) void kernel(Args a) {
     float v = 0.0f;
     for (int sp = 0; sp < W; ++sp) v += parts[((size_t)(tl * W + sp) * 16 + jj) * B + b];
     const size_t off = (size_t)b * M.N + row;
-    if (a.f32out)
+    if (XC) {  // written through to memory (y is a later stage's x)
+      const auto ry = rsrc(M.y, (uint32_t)((size_t)B * M.N * (a.f32out ? 4 : 2)));
+      if (a.f32out)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ry, (int)(off * 4), 0, kCoherent);
+      else
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)v), ry, (int)(off * 2), 0,
+                                              kCoherent);
+    } else if (a.f32out) {
       reinterpret_cast<float *>(M.y)[off] = v;
-    else
+    } else {
       reinterpret_cast<_Float16 *>(M.y)[off] = (_Float16)v;
+    }
   }
+}
+
+template <int B, int P, bool MULTI>
+__global__ __launch_bounds__(kThreads) void kernel(Args a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  body<B, P, MULTI>(a, (int)blockIdx.x, lds);
+}
+
+// ---------------------------------------------------------------------------
+// Fused decode stack: one persistent launch runs a sequence of grouped
+// batch-1 GEMV stages (the projections of a decoder's layers in order), with
+// a device-wide barrier between stages instead of a kernel boundary. Each
+// stage is planned exactly as its own grouped launch and its workgroups run
+// the same body, so every output has the bits of separate launches; the
+// launch's workgroups (one per CU, co-resident by cooperative launch) take
+// the stage's planned workgroups round-robin.
+struct Stage {
+  Args a;
+  int grid;  // workgroups the stage was planned for
+};
+
+// A barrier wait gives up after this many polls (about a second) and sets
+// the error word instead of hanging; the results are then invalid.
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+// sync[0]: arrivals (target = workgroups x barriers passed), sync[1]: error.
+// What crosses stages (each stage's y, the next stages' x) is stored and
+// loaded with system-coherent accesses (the body's XC mode), so the barrier
+// needs no cache writeback or invalidation: every thread waits until its
+// stores have completed, then one thread per group arrives (device-scope
+// atomic) and polls the count.
+__device__ inline void grid_sync(uint32_t *sync, uint32_t target) {
+  __builtin_amdgcn_s_waitcnt(0);           // this thread's stores completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);  // no compiler motion across
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t n = 0;
+    while (__hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++n >= kSpinLimit) {
+        __hip_atomic_fetch_or(sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kThreads) void stack_kernel(const Stage *stages, int n_stages,
+                                                         uint32_t *sync) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  for (int s = 0; s < n_stages; ++s) {
+    const Stage &st = stages[s];
+    const int grid = st.grid;
+    for (int vb = (int)blockIdx.x; vb < grid; vb += (int)gridDim.x) {
+      body<1, 3, true, true>(st.a, vb, lds);
+      if (vb + (int)gridDim.x < grid) __syncthreads();  // LDS reused by the next block
+    }
+    grid_sync(sync, (uint32_t)(s + 1) * gridDim.x);
+  }
+}
+
+__global__ void sync_reset_kernel(uint32_t *sync) {
+  if (threadIdx.x < 2) sync[threadIdx.x] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -651,12 +737,14 @@ int pick_splits(int tw, int sc) {
 
 }  // namespace
 
-// Returns QW_ERR_UNSUPPORTED (nothing enqueued) when the shape does not fit
-// this kernel; the caller then uses the vector-ALU kernel.
-qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void *const *ys,
-                 bool f32, int cus, hipStream_t s) {
+// Plans a grouped launch (Args for the whole batch, its grid); returns
+// QW_ERR_UNSUPPORTED when the shape does not fit this kernel. With more
+// workgroups wanted than ``budget``, the group's matrices share the budget
+// in proportion to their tiles (a matrix alone is never cut).
+static qw_status plan(const qw_weight *ws, int count, const uint16_t *x, void *const *ys, bool f32,
+                      int cus, Args &a, int &grid, int budget = 1 << 30) {
   const int K = ws[0].K;
-  if (K % 512 != 0 || B < 1 || B > 8 || count > kMats) return QW_ERR_UNSUPPORTED;
+  if (K % 512 != 0 || count > kMats) return QW_ERR_UNSUPPORTED;
   int na_max = 0;
   for (int i = 0; i < count; ++i) {
     const int npad = ws[i].n_out > 0 ? ws[i].n_out_pad : 0;
@@ -666,7 +754,7 @@ qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void 
   const int xo_len = na_max * kAnchorChunk;
   if (xo_len > kIdxItems * kThreads) return QW_ERR_UNSUPPORTED;
   const int SC = K / 512;
-  Args a{};
+  a = Args{};
   a.count = count;
   a.x = x;
   a.K = K;
@@ -677,7 +765,8 @@ qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void 
   // is grouped with), so a grouped launch gives the bits of separate ones
   const char *wpc = getenv("QW_GEMV_MC_WG_PER_CU");
   const int wgs_per_cu = wpc ? max(1, atoi(wpc)) : 1;
-  int grid = 0, units_max = 0;
+  int units_max = 0;
+  grid = 0;
   for (int i = 0; i < count; ++i) {
     Mat &m = a.m[i];
     m.codes = reinterpret_cast<const uint32_t *>(ws[i].codes);
@@ -691,6 +780,17 @@ qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void 
     m.n_out_pad = ws[i].n_out > 0 ? ws[i].n_out_pad : 0;
     m.tiles = (m.N + 15) / 16;
     m.wg_count = max(1, min(m.tiles, cus * wgs_per_cu));
+  }
+  long want = 0, all_tiles = 0;
+  for (int i = 0; i < count; ++i) {
+    want += a.m[i].wg_count;
+    all_tiles += a.m[i].tiles;
+  }
+  if (count > 1 && want > budget)
+    for (int i = 0; i < count; ++i)
+      a.m[i].wg_count = (int)max(1L, (long)budget * a.m[i].tiles / all_tiles);
+  for (int i = 0; i < count; ++i) {
+    Mat &m = a.m[i];
     m.wg_begin = grid;
     grid += m.wg_count;
     const int tw = (m.tiles + m.wg_count - 1) / m.wg_count;
@@ -700,6 +800,19 @@ qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void 
   a.units_max = units_max;
   for (int i = 0; i < count; ++i)
     if ((long)a.m[i].tiles * (a.m[i].wg_count + 1) >= (1L << 31)) return QW_ERR_UNSUPPORTED;
+  return QW_OK;
+}
+
+// Returns QW_ERR_UNSUPPORTED (nothing enqueued) when the shape does not fit
+// this kernel; the caller then uses the vector-ALU kernel.
+qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void *const *ys,
+                 bool f32, int cus, hipStream_t s) {
+  if (B < 1 || B > 8) return QW_ERR_UNSUPPORTED;
+  const int K = ws[0].K;
+  Args a;
+  int grid = 0;
+  QW_TRY(plan(ws, count, x, ys, f32, cus, a, grid));
+  const int xo_len = a.xo_len, units_max = a.units_max;
   // Widest batch slice whose x (limbs in LDS, raw x in the prologue
   // registers) fits. Batch rows are independent (each is its own row of the
   // product's A operand), so slicing changes no bits; it pays while slices
@@ -736,3 +849,73 @@ qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void 
 
 }  // namespace gemv2m
 }  // namespace qw
+
+// ---------------------------------------------------------------------------
+extern "C" {
+
+size_t qw_stack_plan_bytes(int n_stages) {
+  if (n_stages < 1 || n_stages > QW_STACK_MAX_STAGES) return 0;
+  return (size_t)n_stages * sizeof(qw::gemv2m::Stage);
+}
+
+qw_status qw_stack_prepare(const qw_stack_stage *stages, int n_stages, void *plan, qw_stack *out) {
+  using namespace qw;
+  using namespace qw::gemv2m;
+  if (!stages || !plan || !out || n_stages < 1 || n_stages > QW_STACK_MAX_STAGES) return QW_ERR_INVALID_ARG;
+  if (!aligned16(plan)) return QW_ERR_ALIGNMENT;
+  int cus = 0;
+  QW_TRY(current_device(&cus));
+  std::vector<Stage> host((size_t)n_stages);
+  size_t lds_max = 0;
+  for (int i = 0; i < n_stages; ++i) {
+    const qw_stack_stage &sg = stages[i];
+    if (sg.count < 1 || sg.count > kMats || !sg.x) return QW_ERR_INVALID_ARG;
+    if (sg.y_dtype != QW_DT_F16 && sg.y_dtype != QW_DT_F32) return QW_ERR_INVALID_ARG;
+    if (!aligned16(sg.x)) return QW_ERR_ALIGNMENT;
+    for (int m = 0; m < sg.count; ++m) {
+      QW_TRY(check_weight_view(&sg.w[m], QW_FMT_2BIT_G32, sg.w[0].K));
+      if (!sg.y[m]) return QW_ERR_INVALID_ARG;
+      if (!aligned16(sg.y[m])) return QW_ERR_ALIGNMENT;
+    }
+    int grid = 0;
+    QW_TRY(qw::gemv2m::plan(sg.w, sg.count, reinterpret_cast<const uint16_t *>(sg.x), sg.y, sg.y_dtype == QW_DT_F32,
+                cus, host[i].a, grid, cus));
+    const int K = sg.w[0].K;
+    if ((long)K > (long)kXItems * kThreads * 8) return QW_ERR_UNSUPPORTED;
+    const size_t lds = lds_layout(1, K, host[i].a.xo_len, host[i].a.units_max).total;
+    if (lds > 160 * 1024) return QW_ERR_UNSUPPORTED;
+    lds_max = max(lds_max, lds);
+    host[i].grid = grid;
+  }
+  QW_HIP_TRY(hipMemcpy(plan, host.data(), host.size() * sizeof(Stage), hipMemcpyHostToDevice));
+  out->plan = plan;
+  out->n_stages = n_stages;
+  out->grid = cus;
+  out->lds = (int32_t)lds_max;
+  return QW_OK;
+}
+
+qw_status qw_stack_run(const qw_stack *st, uint32_t *sync, void *stream) {
+  using namespace qw;
+  using namespace qw::gemv2m;
+  CallScope scope;
+  if (!st || !st->plan || !sync || st->n_stages < 1 || st->n_stages > QW_STACK_MAX_STAGES) return QW_ERR_INVALID_ARG;
+  if (st->grid < 1 || st->lds < 0 || st->lds > 160 * 1024) return QW_ERR_INVALID_ARG;
+  if (!aligned16(sync)) return QW_ERR_ALIGNMENT;
+  int cus = 0;
+  QW_TRY(current_device(&cus));
+  if (st->grid != cus) return QW_ERR_INVALID_ARG;  // prepared for another device
+  hipStream_t s = as_stream(stream);
+  const void *fn = reinterpret_cast<const void *>(&stack_kernel);
+  if (st->lds > 64 * 1024) QW_HIP_TRY(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, st->lds));
+  QW_HIP_TRY(launch(sync_reset_kernel, 1, 64, 0, s, sync));
+  const Stage *plan_p = reinterpret_cast<const Stage *>(st->plan);
+  int n = st->n_stages;
+  uint32_t *sync_p = sync;
+  void *args[] = {(void *)&plan_p, (void *)&n, (void *)&sync_p};
+  // cooperative: every workgroup resident at once, or the launch fails
+  QW_HIP_TRY(launch_cooperative_raw(fn, dim3(st->grid), dim3(kThreads), args, (size_t)st->lds, s));
+  return QW_OK;
+}
+
+}  // extern "C"

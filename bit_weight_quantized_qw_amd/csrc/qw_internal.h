@@ -39,6 +39,10 @@ struct CallScope {
 
 hipError_t launch_raw(const void *fn, dim3 grid, dim3 block, void **argv, size_t lds,
                       hipStream_t s);
+// Cooperative launch (all workgroups co-resident, or it fails) with the
+// call's events recorded on the stream around it.
+hipError_t launch_cooperative_raw(const void *fn, dim3 grid, dim3 block, void **argv, size_t lds,
+                                  hipStream_t s);
 
 template <typename Tup, size_t... I>
 inline void fill_argv(Tup &t, void **argv, std::index_sequence<I...>) {

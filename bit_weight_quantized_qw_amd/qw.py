@@ -27,6 +27,7 @@ EXPORTS = [
     "qw_abi_version", "qw_status_str", "qw_time_next_call", "qw_packed_sizes", "qw_outlier_count",
     "qw_codebook_2bit", "qw_nf4_levels", "qw_select_outliers", "qw_pack",
     "qw_pack_ex", "qw_profile_accumulate", "qw_select_outliers_ex",
+    "qw_stack_plan_bytes", "qw_stack_prepare", "qw_stack_run",
     "qgemv_2bit", "qgemv_nf4", "qgemv_2bit_grouped", "qgemm_prefill",
 ]
 
@@ -51,6 +52,20 @@ class qw_sizes(ctypes.Structure):
     _fields_ = [
         ("codes", ctypes.c_size_t), ("scales", ctypes.c_size_t), ("out_idx", ctypes.c_size_t),
         ("out_w", ctypes.c_size_t), ("out_mask", ctypes.c_size_t), ("n_out_pad", ctypes.c_int32),
+    ]
+
+
+class qw_stack_stage(ctypes.Structure):
+    _fields_ = [
+        ("count", ctypes.c_int32), ("w", qw_weight * 4), ("x", ctypes.c_void_p),
+        ("y", ctypes.c_void_p * 4), ("y_dtype", ctypes.c_int32),
+    ]
+
+
+class qw_stack(ctypes.Structure):
+    _fields_ = [
+        ("plan", ctypes.c_void_p), ("n_stages", ctypes.c_int32), ("grid", ctypes.c_int32),
+        ("lds", ctypes.c_int32),
     ]
 
 
@@ -81,6 +96,9 @@ def lib():
         "qw_pack_ex": (c_i, [c_p, c_i, c_i, W, c_p]),
         "qw_profile_accumulate": (c_i, [c_p, c_i, c_i, c_i, c_p, c_p]),
         "qw_select_outliers_ex": (c_i, [c_p, c_i, c_i, c_i, c_p, ctypes.c_longlong, c_d, c_i, c_p, c_p]),
+        "qw_stack_plan_bytes": (c_sz, [c_i]),
+        "qw_stack_prepare": (c_i, [ctypes.POINTER(qw_stack_stage), c_i, c_p, ctypes.POINTER(qw_stack)]),
+        "qw_stack_run": (c_i, [ctypes.POINTER(qw_stack), c_p, c_p]),
         "qgemv_2bit": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
         "qgemv_nf4": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
         "qgemv_2bit_grouped": (c_i, [W, c_i, c_p, c_i, ctypes.POINTER(c_p), c_i, c_p]),
@@ -360,3 +378,54 @@ def qgemm_prefill(pw, X, out_dtype=None, out=None):
     _check(lib().qgemm_prefill(ctypes.byref(v), _ptr(X), M, _ptr(Y), _dt(Y.dtype), _stream()),
            "qgemm_prefill")
     return Y
+
+
+# ------------------------------------------------------------------ stack
+
+def qw_stack_plan_bytes(n_stages):
+    return int(lib().qw_stack_plan_bytes(int(n_stages)))
+
+
+class Stack:
+    """A prepared fused decode stack (qw_stack_prepare) and its device plan
+    and sync buffers. ``stages`` is a list of (weights, x, ys): up to four
+    PackedWeight (2-bit) sharing the fp16 input x (K,) and their outputs ys
+    ((N_i,) fp16 or fp32 tensors). The tensors are referenced, not copied:
+    each run reads and writes them in place."""
+
+    def __init__(self, stages):
+        import torch
+        n = len(stages)
+        arr = (qw_stack_stage * n)()
+        self._keep = []
+        for i, (ws, x, ys) in enumerate(stages):
+            if not 1 <= len(ws) <= 4 or len(ys) != len(ws):
+                raise ValueError("a stage has 1..4 weights and as many outputs")
+            _need(x, torch.float16, "x", 1)
+            dt = ys[0].dtype
+            for pw, y in zip(ws, ys):
+                _need(y, dt, "y", 1)
+                if pw.K != x.numel() or pw.N != y.numel():
+                    raise ValueError("stage buffers must hold K inputs and N outputs of each weight")
+            arr[i].count = len(ws)
+            for m, (pw, y) in enumerate(zip(ws, ys)):
+                arr[i].w[m] = pw.view()
+                arr[i].y[m] = y.data_ptr()
+            arr[i].x = x.data_ptr()
+            arr[i].y_dtype = QW_DT_F32 if dt == torch.float32 else QW_DT_F16
+            self._keep.append((ws, x, ys))
+        nb = qw_stack_plan_bytes(n)
+        if nb == 0:
+            raise ValueError("too many stages")
+        self.plan = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        self.sync = torch.zeros(4, dtype=torch.int32, device="cuda")
+        self.handle = qw_stack()
+        _check(lib().qw_stack_prepare(arr, n, _ptr(self.plan), ctypes.byref(self.handle)), "qw_stack_prepare")
+
+    def run(self):
+        """Enqueue one run of every stage on the current stream."""
+        _check(lib().qw_stack_run(ctypes.byref(self.handle), _ptr(self.sync), _stream()), "qw_stack_run")
+
+    def error(self):
+        """Non-zero when a barrier wait of the last run gave up (synchronizes)."""
+        return int(self.sync[1].item())

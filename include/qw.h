@@ -252,6 +252,61 @@ qw_status qgemv_2bit_grouped(const qw_weight *ws, int count, const void *x,
                              int B, void *const *ys, qw_dtype y_dtype,
                              void *stream);
 
+/* Fused decode stack (batch 1): a sequence of grouped 2-bit GEMV stages
+ * (for example q/k/v, o, gate/up and down of every layer of a decoder, in
+ * order) run by ONE persistent launch, with a device-wide barrier between
+ * consecutive stages in place of a kernel boundary, so a stage starts only
+ * after every output of the one before is written and visible. Each stage
+ * computes exactly what qgemv_2bit_grouped computes for it on the
+ * matrix-core path (same plan, same summation order: the same bits); the
+ * attention and activation steps between projections are not part of it.
+ * Intended for decode loops where the per-launch cost of hundreds of small
+ * GEMVs per token dominates ("Key v4.0 Innovations" and section 1 of the
+ * OTF-LLM page: decoding is bound by streaming every weight once per
+ * token). */
+#define QW_STACK_MAX_STAGES 4096
+
+typedef struct {
+  int32_t count;      /* matrices sharing x: 1..4 */
+  qw_weight w[4];     /* 2-bit views (device buffers), equal K, K % 512 == 0 */
+  const void *x;      /* device fp16 [K] (batch 1) */
+  void *y[4];         /* device [N_i] outputs, fp16 or fp32 per y_dtype */
+  int32_t y_dtype;    /* QW_DT_F16 or QW_DT_F32 */
+} qw_stack_stage;
+
+/* Host handle of a prepared stack, written by qw_stack_prepare. */
+typedef struct {
+  void *plan;         /* the device plan buffer given to qw_stack_prepare */
+  int32_t n_stages;
+  int32_t grid;       /* workgroups of the persistent launch (one per CU) */
+  int32_t lds;        /* LDS bytes per workgroup */
+} qw_stack;
+
+/* Bytes of the device plan buffer for n_stages stages (0 if out of range). */
+size_t qw_stack_plan_bytes(int n_stages);
+
+/* Plans every stage (as qgemv_2bit_grouped would for batch 1) and copies the
+ * plan to ``plan`` (caller-allocated device memory of qw_stack_plan_bytes,
+ * 16-byte aligned). The weights, x and y pointers are baked into the plan:
+ * later runs read whatever those buffers hold. Unlike every other entry
+ * point this call BLOCKS until the plan is on the device (it copies from
+ * host memory). Errors: INVALID_ARG, ALIGNMENT, UNSUPPORTED (a stage does
+ * not fit the matrix-core kernel: K % 512, K > 49152, LDS), HIP. */
+qw_status qw_stack_prepare(const qw_stack_stage *stages, int n_stages, void *plan,
+                           qw_stack *out);
+
+/* Enqueues one run of a prepared stack on ``stream``: a fill kernel clears
+ * sync, then one cooperative launch with one workgroup per CU runs all
+ * stages.
+ *   sync  device uint32 [2] scratch owned by the caller (16-byte aligned):
+ *         sync[0] counts barrier arrivals; sync[1] is non-zero after the run
+ *         if a barrier wait gave up (about a second per wait; the outputs are
+ *         then invalid). Runs that share a sync buffer must not overlap.
+ * Errors: INVALID_ARG (also a handle prepared on a device with another CU
+ * count), ALIGNMENT, HIP (including a cooperative launch the device
+ * refuses). */
+qw_status qw_stack_run(const qw_stack *st, uint32_t *sync, void *stream);
+
 /* Prefill GEMM: Y[m][n] = sum_k X[m][k] w_bf16[n][k] with
  * w_bf16 = bf16(fp32(S*C[q]+Z)) (one fused multiply-add, then nearest-even)
  * for 2-bit, bf16(fp32(absmax*L[q])) for NF4; 2-bit anchor columns use
