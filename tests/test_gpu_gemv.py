@@ -42,7 +42,7 @@ def test_gemv_2bit_single_layer_2048():
     np.testing.assert_array_equal(y16.astype(np.float16), y32.astype(np.float16))
 
 
-@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_gemv_2bit_14b_shape_with_anchors(B):
     W = inputs.weight(13824, 5120, workload=3)
     X = inputs.profile(256, 5120, workload=3)
@@ -175,6 +175,16 @@ def test_gemv_nf4_one_hot_reads_columns():
     L = oracle.nf4_levels().astype(np.float64)
     np.testing.assert_array_equal(y[0], (a[:, 7 // 64].astype(np.float64) * L[q[:, 7]]).astype(np.float32))
     np.testing.assert_array_equal(y[1], (a[:, 300 // 64].astype(np.float64) * L[q[:, 300]]).astype(np.float32))
+
+
+@pytest.mark.parametrize("B", [5, 6, 7])
+def test_gemv_nf4_batch_slices(B):
+    """Batches cut into 4/2/1-row launches: every row as the oracle."""
+    W = inputs.weight(1000, 4096, workload=79)
+    x = inputs.act_f16(B, 4096, workload=79)
+    q, a = oracle.quantize_nf4(W)
+    e = norm_err(_run_nf4(W, x, f32=True), oracle.gemv_nf4_ref(x, q, a))
+    assert e <= TOL, e
 
 
 def test_gemv_nf4_fp16_out_is_rounded_fp32_out():
