@@ -88,6 +88,9 @@ struct Args {
   int f32out;
   int xo_len;         // anchor index slots in LDS (multiple of 96)
   int units_max;      // max tiles per workgroup * W (partials in LDS)
+  int xraw;           // 1: raw x copied to LDS for the anchor gather; 0:
+                      // anchors gathered from global x (frees B*(K+8)*2
+                      // bytes of LDS so wider batches fit one pass)
 };
 
 // LDS layout, bytes:
@@ -96,13 +99,14 @@ struct Args {
 //   coef   [B][G] float4   {2 d1 2^-s, d3 2^-s, C0 X_g, X_g}
 //   aidx   [xo_len] int32  anchor channels (entries past n_out unused)
 //   xo     [B][xo_len] fp16 x at the anchor channels, zero past n_out
-//   xraw   [B][K + 8] fp16 x as given, 8 zeros after each row (read at K)
+//   xraw   [B][K + 8] fp16 x as given, 8 zeros after each row (read at K);
+//          absent when the anchors are gathered from global x
 //   parts  [units_max][16][B] float  partial row sums of the units
 struct Lds {
   size_t limbs, zero, coef, aidx, xo, xraw, parts, total;
 };
 
-__host__ __device__ inline Lds lds_layout(int B, int K, int xo_len, int units_max) {
+__host__ __device__ inline Lds lds_layout(int B, int K, int xo_len, int units_max, int xraw = 1) {
   const size_t G = (size_t)K / 32;
   Lds l;
   l.limbs = 0;
@@ -111,7 +115,7 @@ __host__ __device__ inline Lds lds_layout(int B, int K, int xo_len, int units_ma
   l.aidx = l.coef + (size_t)B * G * 16;
   l.xo = l.aidx + (((size_t)xo_len * 4 + 15) & ~(size_t)15);
   l.xraw = l.xo + (((size_t)B * xo_len * 2 + 15) & ~(size_t)15);
-  l.parts = l.xraw + (size_t)B * (K + 8) * 2;
+  l.parts = l.xraw + (xraw ? (size_t)B * (K + 8) * 2 : 0);
   l.total = l.parts + (size_t)units_max * 16 * B * 4;
   return l;
 }
@@ -226,7 +230,9 @@ __device__ inline T sel4(int i, T v0, T v1, T v2, T v3) {
 
 // One workgroup's share (workgroup index bid of the launch the Args were
 // planned for) of a grouped GEMV, with the group's LDS at lds.
-template <int B, int P, bool MULTI, bool XC = false>
+// XR: raw x kept in LDS for the anchor gather (a.xraw == 1); false only for
+// batches that fit one pass without it.
+template <int B, int P, bool MULTI, bool XC = false, bool XR = true>
 __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -262,7 +268,7 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
   const int L = SC / W;
   const int NA = (M.n_out_pad + kAnchorChunk - 1) / kAnchorChunk;
   const int n_units = (t1 - t0) * W;
-  const Lds lay = lds_layout(B, K, a.xo_len, a.units_max);
+  const Lds lay = lds_layout(B, K, a.xo_len, a.units_max, XR ? 1 : 0);
   uint8_t *limbs = lds + lay.limbs;
   uint8_t *zero = lds + lay.zero;
   float4 *coef = reinterpret_cast<float4 *>(lds + lay.coef);
@@ -389,7 +395,7 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
       const int gr = bg - b * G;
         const uint32_t om = (mk[q] >> (qt * 8)) & 0xFFu;
         uint32_t d[4] = {xv[q][0], xv[q][1], xv[q][2], xv[q][3]};
-        if (ok) {
+        if (ok && XR) {
           uint32_t *raw = reinterpret_cast<uint32_t *>(xraw + (size_t)b * KX + gr * 32 + qt * 8);
 #pragma unroll
           for (int i = 0; i < 4; ++i) raw[i] = d[i];
@@ -437,7 +443,7 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
       }
     }
     if (threadIdx.x < 8) reinterpret_cast<uint32_t *>(zero)[threadIdx.x] = 0u;
-    if (threadIdx.x < 8 * B) xraw[(threadIdx.x >> 3) * KX + K + (threadIdx.x & 7)] = 0;
+    if (XR && threadIdx.x < 8 * B) xraw[(threadIdx.x >> 3) * KX + K + (threadIdx.x & 7)] = 0;
 #pragma unroll
     for (int q = 0; q < kIdxItems; ++q) {
       const int o = q * kThreads + (int)threadIdx.x;
@@ -459,8 +465,19 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
   if (a.xo_len > 0) {  // uniform
     for (int o = threadIdx.x; o < a.xo_len; o += kThreads) {
       const uint32_t ci = o < M.n_out ? min((uint32_t)aidx_l[o], (uint32_t)K) : (uint32_t)K;
+      if (XR) {
 #pragma unroll
-      for (int b = 0; b < B; ++b) xo[b * a.xo_len + o] = xraw[(size_t)b * KX + ci];
+        for (int b = 0; b < B; ++b) xo[b * a.xo_len + o] = xraw[(size_t)b * KX + ci];
+      } else {
+        // from global x: one 2-byte load per (row, anchor), all in flight;
+        // past n_out an out-of-range offset reads zero
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+          const uint32_t off = ci < (uint32_t)K ? (uint32_t)(b * K + (int)ci) * 2u : kOob;
+          xo[b * a.xo_len + o] =
+              (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r_x, (int)off, 0, XC ? kCoherent : 0);
+        }
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
@@ -618,10 +635,10 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
   }
 }
 
-template <int B, int P, bool MULTI>
+template <int B, int P, bool MULTI, bool XR = true>
 __global__ __launch_bounds__(kThreads) void kernel(Args a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  body<B, P, MULTI>(a, (int)blockIdx.x, lds);
+  body<B, P, MULTI, false, XR>(a, (int)blockIdx.x, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -689,14 +706,23 @@ __global__ void sync_reset_kernel(uint32_t *sync) {
 
 namespace {
 
-template <int B, int P, bool MULTI>
-qw_status launch_bpm(const Args &a, int grid, size_t lds, hipStream_t s) {
+template <int B, int P, bool MULTI, bool XR>
+qw_status launch_bpmx(const Args &a, int grid, size_t lds, hipStream_t s) {
   if (lds > 64 * 1024) {
-    QW_HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(&kernel<B, P, MULTI>),
+    QW_HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(&kernel<B, P, MULTI, XR>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
   }
-  QW_HIP_TRY(launch(kernel<B, P, MULTI>, grid, kThreads, lds, s, a));
+  QW_HIP_TRY(launch(kernel<B, P, MULTI, XR>, grid, kThreads, lds, s, a));
   return QW_OK;
+}
+
+// Batches below 5 always fit with the raw x copy (no variant without it).
+template <int B, int P, bool MULTI>
+qw_status launch_bpm(const Args &a, int grid, size_t lds, hipStream_t s) {
+  if constexpr (B >= 5) {
+    if (!a.xraw) return launch_bpmx<B, P, MULTI, false>(a, grid, lds, s);
+  }
+  return launch_bpmx<B, P, MULTI, true>(a, grid, lds, s);
 }
 
 template <int B, int P>
@@ -760,6 +786,7 @@ static qw_status plan(const qw_weight *ws, int count, const uint16_t *x, void *c
   a.K = K;
   a.f32out = f32 ? 1 : 0;
   a.xo_len = xo_len;
+  a.xraw = 1;
   // every matrix is planned as if it were launched alone (its workgroup
   // count, hence its K split and summation order, do not depend on what it
   // is grouped with), so a grouped launch gives the bits of separate ones
@@ -818,12 +845,19 @@ qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void 
   // product's A operand), so slicing changes no bits; it pays while slices
   // hold at least two rows (a pass per single row is slower than the
   // vector-ALU kernel).
-  auto fits = [&](int b) {
+  auto fits = [&](int b, int xr) {
     return (long)b * K <= (long)kXItems * kThreads * 8 &&
-           lds_layout(b, K, xo_len, units_max).total <= 160 * 1024;
+           lds_layout(b, K, xo_len, units_max, xr).total <= 160 * 1024;
   };
+  // without the raw x copy the whole batch may fit one pass (the weights
+  // stream once instead of once per slice); with it the anchor gather reads
+  // LDS instead of memory, so it is kept whenever the batch fits with it
   int bmax = B;
-  while (bmax > 0 && !fits(bmax)) --bmax;
+  if (!fits(B, 1) && fits(B, 0)) {
+    a.xraw = 0;
+  } else {
+    while (bmax > 0 && !fits(bmax, 1)) --bmax;
+  }
   if (bmax < B && bmax < 2) return QW_ERR_UNSUPPORTED;
   const int n_slices = (B + bmax - 1) / bmax;
   // 3 ring slots per wave: measured on MI355X, the deep ring (6 slots up to
@@ -840,7 +874,7 @@ qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void 
     as.x = x + (size_t)b0 * K;
     for (int i = 0; i < count; ++i)
       as.m[i].y = reinterpret_cast<char *>(ys[i]) + (size_t)b0 * ws[i].N * esz;
-    const size_t lds = lds_layout(bs, K, xo_len, units_max).total;
+    const size_t lds = lds_layout(bs, K, xo_len, units_max, a.xraw).total;
     QW_TRY(launch_b(as, bs, deep, grid, lds, s));
     b0 += bs;
   }

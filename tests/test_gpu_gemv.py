@@ -55,6 +55,23 @@ def test_gemv_2bit_14b_shape_with_anchors(B):
     assert e <= TOL
 
 
+@pytest.mark.parametrize("B", [5, 8])
+def test_gemv_2bit_wide_batch_rows_equal_single_rows(B, monkeypatch):
+    """A batch that fits one matrix-core pass only without the raw x copy in
+    LDS (anchors then gathered from global x) gives every row the bits of
+    that row computed alone."""
+    W = inputs.weight(4096, 5120, workload=81)
+    X = inputs.profile(64, 5120, workload=81)
+    idx = oracle.select_outliers(W, X, 0.035)
+    x = inputs.act_f16(B, 5120, workload=81)
+    pw = _packed_2bit(W, idx)
+    monkeypatch.setenv("QW_GEMV_VALU", "0")
+    yB = _run_2bit(pw, x, f32=True)
+    for b in range(B):
+        np.testing.assert_array_equal(yB[b], _run_2bit(pw, x[b:b + 1], f32=True)[0], err_msg=f"row {b}")
+    assert norm_err(yB, _ref_2bit(W, x, idx)) <= TOL
+
+
 @pytest.mark.parametrize("N,K,n_anchor", [(1, 32, 0), (7, 96, 2), (33, 1056, 5), (130, 2080, 0),
                                           (64, 3072, 40), (5, 27648, 967), (300, 27648, 967)])
 @pytest.mark.parametrize("B", [1, 2, 4])
