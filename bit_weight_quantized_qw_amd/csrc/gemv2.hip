@@ -124,8 +124,11 @@ qw_status launch(const qw_weight *ws, int count, const void *x, int B, void *con
   // fits it; otherwise batch rows go through vector-ALU kernels of width 4,
   // 2 and 1 (e.g. 7 = 4 + 2 + 1).
   // Path choice (measured on MI355X): the matrix-core kernel for batches of
-  // two or more, and at batch 1 for K <= 8192 (beyond, the vector-ALU kernel
-  // is faster at batch 1). QW_GEMV_VALU=1 forces the vector-ALU kernel and
+  // two or more, and at batch 1 for K <= 8192; beyond, at batch 1, for
+  // matrices whose 16-row tiles spread evenly over the CUs (at least 3/4 of
+  // the slots of the busiest round filled: 4096 or 8192 rows on 256 CUs),
+  // the vector-ALU kernel (which splits rows, not tiles) otherwise (5120
+  // rows: 320 tiles). QW_GEMV_VALU=1 forces the vector-ALU kernel and
   // QW_GEMV_VALU=0 the matrix-core one where it applies (for tests).
   // The choice is made per matrix (a grouped call gives the bits of
   // separate calls): the matrices that take the matrix-core kernel go out as
@@ -136,7 +139,10 @@ qw_status launch(const qw_weight *ws, int count, const void *x, int B, void *con
   void *mc_y[kMaxMats], *va_y[kMaxMats];
   int n_mc = 0, n_va = 0;
   for (int i = 0; i < count; ++i) {
-    const bool mc = force == 0 || (force < 0 && (B >= 2 || K <= 8192));
+    const long tiles = (ws[i].N + 15) / 16, wgs = max(1L, min(tiles, (long)cus));
+    const long slots = (tiles + wgs - 1) / wgs * wgs;
+    const bool balanced = 4 * tiles >= 3 * slots;
+    const bool mc = force == 0 || (force < 0 && (B >= 2 || K <= 8192 || balanced));
     if (mc) {
       mc_w[n_mc] = ws[i];
       mc_y[n_mc++] = ys[i];

@@ -41,6 +41,7 @@
 // and are added in a fixed order.
 #include <stdlib.h>
 
+#include <mutex>
 #include <vector>
 
 #include "qw_internal.h"
@@ -72,19 +73,24 @@ struct Mat {
   const uint32_t *sz;     // [N][K/32]: fp16 S | fp16 Z << 16
   const uint32_t *mask;   // [K/32] anchor-channel bits, null without anchors
   const int32_t *idx;     // [n_out]
-  const uint16_t *wo;     // [N][n_out_pad] fp16
+  const uint16_t *wo;     // [N][ld_a] fp16
   void *y;                // [B][N]
-  int N, n_out, n_out_pad;
+  int N, n_out, n_out_pad; // anchors of this launch's share (padded to 8)
   int wg_begin, wg_count;  // this matrix's workgroups
   int tiles;               // ceil(N / 16)
   int W;                   // waves per tile (K splits); divides K/512
+  int kbase;               // first channel of this K part (0 unless split);
+                           // codes, sz and mask already point at it
+  int ld_a;                // anchors per weight row (row stride of wo)
+  int abase;               // first anchor of this part; idx and wo point at it
 };
 
 struct Args {
   Mat m[kMats];
   int count;
-  const uint16_t *x;  // [B][K] fp16
-  int K;
+  const uint16_t *x;  // [B][ldk] fp16
+  int K;              // channels per matrix of this launch (a K part when split)
+  int ldk;            // channels per weight row and per x row
   int f32out;
   int xo_len;         // anchor index slots in LDS (multiple of 96)
   int units_max;      // max tiles per workgroup * W (partials in LDS)
@@ -251,12 +257,14 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
     const int32_t *idx;
     const uint16_t *wo;
     void *y;
-    int N, n_out, n_out_pad, wg_begin, wg_count, tiles, W;
+    int N, n_out, n_out_pad, wg_begin, wg_count, tiles, W, kbase, ld_a, abase;
   } M = {QW_SEL(codes), QW_SEL(sz),    QW_SEL(mask),      QW_SEL(idx),      QW_SEL(wo),
          QW_SEL(y),     QW_SEL(N),     QW_SEL(n_out),     QW_SEL(n_out_pad), QW_SEL(wg_begin),
-         QW_SEL(wg_count), QW_SEL(tiles), QW_SEL(W)};
+         QW_SEL(wg_count), QW_SEL(tiles), QW_SEL(W),      QW_SEL(kbase),     QW_SEL(ld_a),
+         QW_SEL(abase)};
 #undef QW_SEL
   const int K = a.K;
+  const int ldk = a.ldk;
   const int G = K >> 5;
   const int SC = K >> 9;
   const int wi = bid - M.wg_begin;
@@ -284,12 +292,14 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
   Stream st{n_units, W, L, NA};
 
   // ---- per-lane load offsets ----
-  const uint32_t rb_c = (uint32_t)K / 4;           // code bytes per row
-  const uint32_t rb_s = (uint32_t)K / 8;           // S/Z bytes per row
-  const uint32_t rb_a = (uint32_t)M.n_out_pad * 2; // anchor bytes per row
-  const uint32_t n_codes = (uint32_t)((size_t)M.N * rb_c);
-  const uint32_t n_sz = (uint32_t)((size_t)M.N * rb_s);
-  const uint32_t n_wo = (uint32_t)((size_t)M.N * rb_a);
+  const uint32_t rb_c = (uint32_t)ldk / 4;         // code bytes per row
+  const uint32_t rb_s = (uint32_t)ldk / 8;         // S/Z bytes per row
+  const uint32_t rb_a = (uint32_t)M.ld_a * 2;      // anchor bytes per row
+  const uint32_t lim_a = (uint32_t)M.n_out_pad * 2; // this part's anchor bytes per row
+  // sizes from the part's first channel (anchor) to the end of the matrix
+  const uint32_t n_codes = (uint32_t)((size_t)M.N * rb_c - (uint32_t)M.kbase / 4);
+  const uint32_t n_sz = (uint32_t)((size_t)M.N * rb_s - (uint32_t)M.kbase / 8);
+  const uint32_t n_wo = (uint32_t)((size_t)M.N * rb_a - (uint32_t)M.abase * 2);
 
   // ring slot = three 16-byte loads per lane. Code step: lane (row j,
   // slot g) takes groups 16 sc + 4g .. +3 of its row: codes bytes [32g, 32g+32)
@@ -324,9 +334,9 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
       v1 = row_ok ? v0 + 16 : kOob;
       v2 = row_ok ? (uint32_t)j * rb_s + 16u * g : kOob;
     } else {
-      v0 = row_ok && pa < rb_a ? (uint32_t)j * rb_a + pa : kOob;
-      v1 = row_ok && pa + 64 < rb_a ? (uint32_t)j * rb_a + pa + 64 : kOob;
-      v2 = row_ok && pa + 128 < rb_a ? (uint32_t)j * rb_a + pa + 128 : kOob;
+      v0 = row_ok && pa < lim_a ? (uint32_t)j * rb_a + pa : kOob;
+      v1 = row_ok && pa + 64 < lim_a ? (uint32_t)j * rb_a + pa + 64 : kOob;
+      v2 = row_ok && pa + 128 < lim_a ? (uint32_t)j * rb_a + pa + 128 : kOob;
     }
     dst.c0 = ld4(r01, v0, s01);
     dst.c1 = ld4(r01, v1, s01);
@@ -335,7 +345,7 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
 
   // ---- prologue loads: x (16 bytes per item), anchor mask, anchor indices ----
   const int n_items = B * G * 4;  // (b, group, quarter)
-  const auto r_x = rsrc(a.x, (uint32_t)((size_t)B * K * 2));
+  const auto r_x = rsrc(a.x, (uint32_t)((size_t)B * ldk * 2));
   const auto r_mask = rsrc(M.mask, M.mask ? (uint32_t)G * 4 : 0u);
   const auto r_idx = rsrc(M.idx, (uint32_t)M.n_out * 4);
   u32x4 xv[kXItems];
@@ -353,7 +363,7 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
 #pragma unroll
       for (int t = 1; t < B; ++t) b += bg >= t * G;
       const int gr = bg - b * G;
-      const uint32_t xoff = ok ? (uint32_t)((b * K + gr * 32 + qt * 8) * 2) : kOob;
+      const uint32_t xoff = ok ? (uint32_t)((b * ldk + M.kbase + gr * 32 + qt * 8) * 2) : kOob;
       xv[q] = XC ? ld4_coherent(r_x, xoff, 0) : ld4(r_x, xoff, 0);
       if (has_mask) mk[q] = ld1(r_mask, ok ? (uint32_t)gr * 4 : kOob, 0);
     }
@@ -464,7 +474,8 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
   // at K), then a second LDS-only barrier (none without anchors)
   if (a.xo_len > 0) {  // uniform
     for (int o = threadIdx.x; o < a.xo_len; o += kThreads) {
-      const uint32_t ci = o < M.n_out ? min((uint32_t)aidx_l[o], (uint32_t)K) : (uint32_t)K;
+      // XR only for unsplit launches (ldk == K)
+      const uint32_t ci = o < M.n_out ? min((uint32_t)aidx_l[o], (uint32_t)ldk) : (uint32_t)ldk;
       if (XR) {
 #pragma unroll
         for (int b = 0; b < B; ++b) xo[b * a.xo_len + o] = xraw[(size_t)b * KX + ci];
@@ -473,7 +484,7 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
         // past n_out an out-of-range offset reads zero
 #pragma unroll
         for (int b = 0; b < B; ++b) {
-          const uint32_t off = ci < (uint32_t)K ? (uint32_t)(b * K + (int)ci) * 2u : kOob;
+          const uint32_t off = ci < (uint32_t)ldk ? (uint32_t)(b * ldk + (int)ci) * 2u : kOob;
           xo[b * a.xo_len + o] =
               (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r_x, (int)off, 0, XC ? kCoherent : 0);
         }
@@ -716,12 +727,11 @@ qw_status launch_bpmx(const Args &a, int grid, size_t lds, hipStream_t s) {
   return QW_OK;
 }
 
-// Batches below 5 always fit with the raw x copy (no variant without it).
+// Without the raw x copy: wide batches that fit one pass only so, and every
+// K-split launch (a part's LDS holds only its own channels of x).
 template <int B, int P, bool MULTI>
 qw_status launch_bpm(const Args &a, int grid, size_t lds, hipStream_t s) {
-  if constexpr (B >= 5) {
-    if (!a.xraw) return launch_bpmx<B, P, MULTI, false>(a, grid, lds, s);
-  }
+  if (!a.xraw) return launch_bpmx<B, P, MULTI, false>(a, grid, lds, s);
   return launch_bpmx<B, P, MULTI, true>(a, grid, lds, s);
 }
 
@@ -784,6 +794,7 @@ static qw_status plan(const qw_weight *ws, int count, const uint16_t *x, void *c
   a.count = count;
   a.x = x;
   a.K = K;
+  a.ldk = K;
   a.f32out = f32 ? 1 : 0;
   a.xo_len = xo_len;
   a.xraw = 1;
@@ -805,6 +816,7 @@ static qw_status plan(const qw_weight *ws, int count, const uint16_t *x, void *c
     m.N = ws[i].N;
     m.n_out = ws[i].n_out;
     m.n_out_pad = ws[i].n_out > 0 ? ws[i].n_out_pad : 0;
+    m.ld_a = m.n_out_pad;
     m.tiles = (m.N + 15) / 16;
     m.wg_count = max(1, min(m.tiles, cus * wgs_per_cu));
   }
@@ -830,42 +842,231 @@ static qw_status plan(const qw_weight *ws, int count, const uint16_t *x, void *c
   return QW_OK;
 }
 
-// Returns QW_ERR_UNSUPPORTED (nothing enqueued) when the shape does not fit
-// this kernel; the caller then uses the vector-ALU kernel.
-qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void *const *ys,
-                 bool f32, int cus, hipStream_t s) {
-  if (B < 1 || B > 8) return QW_ERR_UNSUPPORTED;
-  const int K = ws[0].K;
+// ---------------------------------------------------------------------------
+// K split. A matrix's channels are cut into ks equal parts (whole super-chunks
+// of 512) and its anchor chunks into ks runs; each part is one matrix of a
+// grouped launch (up to kMats parts per launch, several launches beyond)
+// whose rows are fp32 partial sums, written to a workspace; a last kernel
+// adds the parts in order into y. It lets batches whose x (limbs for every
+// row) does not fit one workgroup's LDS stream the weights once, instead of
+// once per batch row through the vector-ALU kernel.
+
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float *parts, int ks, int n, void *y,
+                                                           int f32) {
+  const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  if (i >= n) return;
+  float v = parts[i];
+  for (int p = 1; p < ks; ++p) v += parts[(size_t)p * n + i];
+  if (f32)
+    reinterpret_cast<float *>(y)[i] = v;
+  else
+    reinterpret_cast<_Float16 *>(y)[i] = (_Float16)v;
+}
+
+namespace {
+
+constexpr int kMaxSplit = 8;
+
+int env_int(const char *name, int dflt) {
+  const char *v = getenv(name);
+  return v ? atoi(v) : dflt;
+}
+
+bool fits_one_wg(int b, int K, int xo_len, int units_max, int xr) {
+  return (long)b * K <= (long)kXItems * kThreads * 8 &&
+         lds_layout(b, K, xo_len, units_max, xr).total <= 160 * 1024;
+}
+
+// Batch slices of an unsplit launch planned as `a` (0: none fits), and
+// whether they keep the raw x copy. Without the raw x copy the whole batch
+// may fit one pass (the weights stream once instead of once per slice); with
+// it the anchor gather reads LDS instead of memory, so it is kept whenever
+// the batch fits with it. Slices of one row are left to the vector-ALU
+// kernel (faster there).
+int unsplit_slices(const Args &a, int B, int *xraw, int *bmax_out) {
+  int bmax = B;
+  *xraw = 1;
+  if (!fits_one_wg(B, a.K, a.xo_len, a.units_max, 1) && fits_one_wg(B, a.K, a.xo_len, a.units_max, 0)) {
+    *xraw = 0;
+  } else {
+    while (bmax > 0 && !fits_one_wg(bmax, a.K, a.xo_len, a.units_max, 1)) --bmax;
+  }
+  *bmax_out = bmax;
+  if (bmax < B && bmax < 2) return 0;
+  return (B + bmax - 1) / bmax;
+}
+
+// Part p of ks: the weight view with its channels and its run of anchor
+// chunks, planned alone; its Mat is a.m[0].
+qw_status plan_part(const qw_weight &w, int ks, int p, const uint16_t *x, int cus, Args &a, int &grid) {
+  qw_weight pw = w;
+  pw.K = w.K / ks;
+  void *dummy = nullptr;
+  QW_TRY(plan(&pw, 1, x, &dummy, true, cus, a, grid));
+  Mat &m = a.m[0];
+  const int kp = pw.K;
+  m.kbase = p * kp;
+  m.codes += (size_t)p * kp / 16;
+  m.sz += (size_t)p * kp / 32;
+  if (m.mask) m.mask += (size_t)p * kp / 32;
+  const int na = (m.ld_a + kAnchorChunk - 1) / kAnchorChunk;
+  const int a0 = p * na / ks, a1 = (p + 1) * na / ks;
+  m.abase = a0 * kAnchorChunk;
+  m.n_out = max(0, min(m.n_out, a1 * kAnchorChunk) - m.abase);
+  m.n_out_pad = max(0, min(m.n_out_pad, a1 * kAnchorChunk) - m.abase);
+  if (m.n_out == 0) m.n_out_pad = 0;
+  m.idx += m.abase;
+  m.wo += m.abase;
+  a.ldk = w.K;
+  a.xraw = 0;
+  a.f32out = 1;
+  a.xo_len = (m.n_out_pad + kAnchorChunk - 1) / kAnchorChunk * kAnchorChunk;
+  return QW_OK;
+}
+
+// K parts for one matrix at batch B: 1 = unsplit, 0 = this kernel does not
+// take the shape. Measured on MI355X, a split pays only where no unsplit
+// pass of two or more batch rows fits (the split's extra workgroups each
+// prepare their share of x for the whole batch, and the parts cost one more
+// launch), and there the fewest parts that fit are fastest. QW_GEMV_SPLIT=n
+// forces n parts where n is valid (tests).
+int choose_split(const qw_weight &w, const uint16_t *x, int B, int cus) {
+  const int K = w.K;
+  if (K % 512 != 0) return 0;
   Args a;
   int grid = 0;
-  QW_TRY(plan(ws, count, x, ys, f32, cus, a, grid));
-  const int xo_len = a.xo_len, units_max = a.units_max;
-  // Widest batch slice whose x (limbs in LDS, raw x in the prologue
-  // registers) fits. Batch rows are independent (each is its own row of the
-  // product's A operand), so slicing changes no bits; it pays while slices
-  // hold at least two rows (a pass per single row is slower than the
-  // vector-ALU kernel).
-  auto fits = [&](int b, int xr) {
-    return (long)b * K <= (long)kXItems * kThreads * 8 &&
-           lds_layout(b, K, xo_len, units_max, xr).total <= 160 * 1024;
-  };
-  // without the raw x copy the whole batch may fit one pass (the weights
-  // stream once instead of once per slice); with it the anchor gather reads
-  // LDS instead of memory, so it is kept whenever the batch fits with it
-  int bmax = B;
-  if (!fits(B, 1) && fits(B, 0)) {
-    a.xraw = 0;
-  } else {
-    while (bmax > 0 && !fits(bmax, 1)) --bmax;
+  void *dummy = nullptr;
+  if (plan(&w, 1, x, &dummy, true, cus, a, grid) != QW_OK) return 0;
+  int xr = 1, bmax = 0;
+  const int ns = unsplit_slices(a, B, &xr, &bmax);
+  const int forced = env_int("QW_GEMV_SPLIT", 0);
+  if (ns > 0 && forced <= 1) return 1;
+  const int SC = K / 512;
+  int first = 0;
+  for (int ks = 2; ks <= kMaxSplit; ++ks) {
+    if (SC % ks != 0) continue;
+    Args ap;
+    int gp = 0;
+    if (plan_part(w, ks, 0, x, cus, ap, gp) != QW_OK) continue;
+    // part 0 holds the longest anchor run
+    if (!fits_one_wg(B, ap.K, ap.xo_len, ap.units_max, 0)) continue;
+    if (forced == ks) return ks;
+    if (first == 0) first = ks;
   }
-  if (bmax < B && bmax < 2) return QW_ERR_UNSUPPORTED;
-  const int n_slices = (B + bmax - 1) / bmax;
+  if (ns > 0) return 1;
+  return first;
+}
+
+// Workspace of the K split: one buffer per (device, stream), grown on demand
+// and kept until the process ends. Work on one stream runs in order, so its
+// calls can share the buffer; a replaced buffer is kept too, since a graph
+// captured earlier may still hold its address. Growth calls hipMalloc, so it
+// is refused while the stream is being captured (an eager call of the same
+// shape before the capture sizes the buffer).
+struct SplitWs {
+  int dev;
+  hipStream_t s;
+  void *p;
+  size_t bytes;
+};
+std::mutex g_ws_mu;
+std::vector<SplitWs> g_ws;
+std::vector<void *> g_ws_retired;
+
+qw_status split_workspace(hipStream_t s, size_t bytes, float **out) {
+  int dev = 0;
+  QW_HIP_TRY(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  SplitWs *e = nullptr;
+  for (auto &w : g_ws)
+    if (w.dev == dev && w.s == s) e = &w;
+  if (e && e->bytes >= bytes) {
+    *out = reinterpret_cast<float *>(e->p);
+    return QW_OK;
+  }
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  QW_HIP_TRY(hipStreamIsCapturing(s, &cs));
+  if (cs != hipStreamCaptureStatusNone) return QW_ERR_UNSUPPORTED;
+  const size_t grow = e ? max(bytes, 2 * e->bytes) : max(bytes, (size_t)1 << 20);
+  void *p = nullptr;
+  QW_HIP_TRY(hipMalloc(&p, grow));
+  if (e) {
+    g_ws_retired.push_back(e->p);
+    e->p = p;
+    e->bytes = grow;
+  } else {
+    g_ws.push_back(SplitWs{dev, s, p, grow});
+  }
+  *out = reinterpret_cast<float *>(p);
+  return QW_OK;
+}
+
+bool deep_ring() {
   // 3 ring slots per wave: measured on MI355X, the deep ring (6 slots up to
   // batch 2, 4 beyond) is slower with weights coming from HBM even for waves
   // with many steps; QW_GEMV_MC_DEEP=1 selects it (tests check both give the
   // same bits)
-  const char *dv = getenv("QW_GEMV_MC_DEEP");
-  const bool deep = dv ? atoi(dv) != 0 : false;
+  return env_int("QW_GEMV_MC_DEEP", 0) != 0;
+}
+
+qw_status launch_split(const qw_weight &w, int ks, const uint16_t *x, int B, void *y, bool f32, int cus,
+                       hipStream_t s) {
+  const size_t plane = (size_t)B * w.N;
+  if (plane >= (1u << 31) / 2) return QW_ERR_UNSUPPORTED;
+  Args parts_a[kMaxSplit];
+  int grid_p = 0;
+  for (int p = 0; p < ks; ++p) QW_TRY(plan_part(w, ks, p, x, cus, parts_a[p], grid_p));
+  float *parts = nullptr;
+  QW_TRY(split_workspace(s, (size_t)ks * plane * sizeof(float), &parts));
+  const bool deep = deep_ring();
+  qw_status st = QW_OK;
+  for (int p0 = 0; p0 < ks && st == QW_OK; p0 += kMats) {
+    Args a = parts_a[p0];
+    a.count = min(kMats, ks - p0);
+    int xo_len = 0;
+    for (int i = 0; i < a.count; ++i) {
+      a.m[i] = parts_a[p0 + i].m[0];
+      a.m[i].y = parts + (size_t)(p0 + i) * plane;
+      a.m[i].wg_begin = i * grid_p;
+      xo_len = max(xo_len, parts_a[p0 + i].xo_len);
+    }
+    a.xo_len = xo_len;
+    const size_t lds = lds_layout(B, a.K, a.xo_len, a.units_max, 0).total;
+    st = launch_b(a, B, deep, grid_p * a.count, lds, s);
+  }
+  if (st == QW_OK &&
+      launch(split_reduce_kernel, (unsigned)((plane + 255) / 256), 256, 0, s, (const float *)parts, ks,
+             (int)plane, y, f32 ? 1 : 0) != hipSuccess)
+    st = QW_ERR_HIP;
+  return st;
+}
+
+}  // namespace
+
+// Returns QW_ERR_UNSUPPORTED (nothing enqueued) when the shape does not fit
+// this kernel; the caller then uses the vector-ALU kernel. A grouped call
+// whose matrices would be split alone is refused too (the caller then
+// launches them one by one), so that it gives the bits of separate calls.
+qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void *const *ys,
+                 bool f32, int cus, hipStream_t s) {
+  if (B < 1 || B > 8) return QW_ERR_UNSUPPORTED;
+  for (int i = 0; i < count; ++i) {
+    const int ks = choose_split(ws[i], x, B, cus);
+    if (ks == 0) return QW_ERR_UNSUPPORTED;
+    if (ks > 1) return count == 1 ? launch_split(ws[0], ks, x, B, ys[0], f32, cus, s) : QW_ERR_UNSUPPORTED;
+  }
+  const int K = ws[0].K;
+  Args a;
+  int grid = 0;
+  QW_TRY(plan(ws, count, x, ys, f32, cus, a, grid));
+  // Widest batch slice whose x (limbs in LDS, raw x in the prologue
+  // registers) fits. Batch rows are independent (each is its own row of the
+  // product's A operand), so slicing changes no bits.
+  int xr = 1, bmax = 0;
+  const int n_slices = unsplit_slices(a, B, &xr, &bmax);
+  if (n_slices == 0) return QW_ERR_UNSUPPORTED;
+  a.xraw = xr;
+  const bool deep = deep_ring();
   const size_t esz = f32 ? 4 : 2;
   int b0 = 0;
   for (int sl = 0; sl < n_slices; ++sl) {
@@ -874,7 +1075,7 @@ qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void 
     as.x = x + (size_t)b0 * K;
     for (int i = 0; i < count; ++i)
       as.m[i].y = reinterpret_cast<char *>(ys[i]) + (size_t)b0 * ws[i].N * esz;
-    const size_t lds = lds_layout(bs, K, xo_len, units_max, a.xraw).total;
+    const size_t lds = lds_layout(bs, K, a.xo_len, a.units_max, a.xraw).total;
     QW_TRY(launch_b(as, bs, deep, grid, lds, s));
     b0 += bs;
   }

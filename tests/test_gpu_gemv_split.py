@@ -1,0 +1,129 @@
+"""GPU parity of the K-split matrix-core 2-bit GEMV. A matrix's channels are
+cut into equal parts of whole 512-channel super-chunks and its anchor chunks
+into runs, one part per matrix of a grouped launch (two launches beyond four
+parts); the parts' fp32 partial rows are added in order. Part counts forced
+through QW_GEMV_SPLIT on small ragged shapes (parts with and without
+anchors, batches 1-8), a one-hot check that every part reads its own
+channels, and the automatic choice at 5120x27648 with 967 anchors (where
+batches of 2-8 only fit as parts), all against the fp64 oracle."""
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_weight_quantized_qw_amd import inputs, qw
+from gpu_util import TOL, norm_err, to_dev, f16_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _packed(W, idx):
+    idd = to_dev(np.asarray(idx, np.int32)) if idx is not None and len(idx) else None
+    return qw.qw_pack(to_dev(W), qw.QW_FMT_2BIT_G32, idd)
+
+
+def _run(pw, x16, f32):
+    import torch
+    y = qw.qgemv_2bit(pw, f16_dev(x16), out_dtype=torch.float32 if f32 else torch.float16)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy()
+
+
+def _anchors(K, n, seed):
+    if n == 0:
+        return None
+    return np.sort(np.random.default_rng(seed).choice(K, n, replace=False)).astype(np.int32)
+
+
+@pytest.mark.parametrize("N,K,n_anchor,ks", [
+    (200, 3072, 107, 2), (200, 3072, 107, 3), (200, 3072, 107, 6),
+    (77, 3072, 614, 3), (77, 3072, 614, 6),
+    (48, 4608, 0, 3), (33, 6144, 2000, 4), (33, 6144, 2000, 6)])
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_forced_split_matches_oracle(N, K, n_anchor, ks, B, monkeypatch):
+    monkeypatch.setenv("QW_GEMV_VALU", "0")
+    monkeypatch.setenv("QW_GEMV_SPLIT", str(ks))
+    W = inputs.weight(N, K, workload=90)
+    idx = _anchors(K, n_anchor, N + K)
+    x = inputs.act_f16(B, K, workload=90)
+    pw = _packed(W, idx)
+    r = oracle.quantize_2bit(W, idx)
+    ref = oracle.gemv_2bit_ref(x, r["q"], r["S"], r["Z"], r["idx"], r["W_O"])
+    y32 = _run(pw, x, True)
+    y16 = _run(pw, x, False)
+    e = norm_err(y32, ref)
+    print(f"{N}x{K} anchors={n_anchor} parts={ks} B={B}: err {e:.3e}")
+    assert e <= TOL
+    # the fp16 output is the fp32 sum of the parts rounded once
+    np.testing.assert_array_equal(y16.astype(np.float16), y32.astype(np.float16))
+
+
+def test_split_parts_read_their_own_channels(monkeypatch):
+    monkeypatch.setenv("QW_GEMV_VALU", "0")
+    monkeypatch.setenv("QW_GEMV_SPLIT", "3")
+    N, K = 40, 3072
+    W = inputs.weight(N, K, workload=91)
+    idx = np.array([5, 700, 1500, 2047, 3000] + list(range(2100, 2400, 3)), np.int32)
+    idx = np.unique(idx)
+    pw = _packed(W, idx)
+    r = oracle.quantize_2bit(W, idx)
+    Wh = oracle.dequant_2bit(r["q"], r["S"], r["Z"])
+    cols = [0, 5, 511, 512, 1023, 1024, 1500, 2047, 2048, 2100, 2103, 2397, 3000, 3071]
+    x = np.zeros((len(cols), K), np.float16)
+    for b, k in enumerate(cols[:8]):
+        x[b, k] = 1
+    x2 = np.zeros((len(cols) - 8, K), np.float16)
+    for b, k in enumerate(cols[8:]):
+        x2[b, k] = 1
+    y = np.concatenate([_run(pw, x[:8], True), _run(pw, x2, True)])
+    pos = {int(c): i for i, c in enumerate(idx)}
+    for b, k in enumerate(cols):
+        ref = r["W_O"][:, pos[k]].astype(np.float64) if k in pos else Wh[:, k]
+        assert norm_err(y[b], ref) <= 1e-6, k
+
+
+def test_split_fp16_inputs_at_extremes(monkeypatch):
+    """Large and tiny inputs through the parts (per-group scaling of x)."""
+    monkeypatch.setenv("QW_GEMV_VALU", "0")
+    monkeypatch.setenv("QW_GEMV_SPLIT", "2")
+    N, K = 64, 2048
+    W = inputs.weight(N, K, workload=92)
+    idx = _anchors(K, 70, 92)
+    pw = _packed(W, idx)
+    r = oracle.quantize_2bit(W, idx)
+    for scale in (1e-4, 3000.0):
+        x = np.clip(inputs.act_f16(2, K, workload=92).astype(np.float32) * scale, -65504, 65504)
+        x = x.astype(np.float16)
+        ref = oracle.gemv_2bit_ref(x, r["q"], r["S"], r["Z"], r["idx"], r["W_O"])
+        e = norm_err(_run(pw, x, True), ref)
+        assert e <= TOL, (scale, e)
+
+
+@pytest.fixture(scope="module")
+def down():
+    N, K = 5120, 27648
+    W = inputs.weight(N, K, workload=4, layer=0, proj=6)
+    X = inputs.profile(256, K, workload=4, layer=0, proj=3)
+    Wd = to_dev(W)
+    idx = qw.qw_select_outliers(Wd, to_dev(X), 0.035)
+    pw = qw.qw_pack(Wd, qw.QW_FMT_2BIT_G32, idx)
+    del Wd
+    rows = np.sort(inputs.rng(4, 0, 6, 5).choice(N, 192, replace=False))
+    r = oracle.quantize_2bit(W[rows], idx.cpu().numpy())
+    return pw, rows, r
+
+
+@pytest.mark.parametrize("B", [1, 2, 5, 8])
+@pytest.mark.parametrize("path", ["auto", "matrix_core"])
+def test_down_projection_batches(down, B, path, monkeypatch):
+    """5120x27648 with 967 anchors: batches of 2-8 run as K parts (their x
+    does not fit one workgroup whole); checked on 192 sampled rows."""
+    if path == "matrix_core":
+        monkeypatch.setenv("QW_GEMV_VALU", "0")
+    pw, rows, r = down
+    x = inputs.act_f16(B, 27648, workload=4, layer=0, proj=9)
+    y = _run(pw, x, True)
+    ref = oracle.gemv_2bit_ref(x, r["q"], r["S"], r["Z"], r["idx"], r["W_O"])
+    e = norm_err(y[:, rows], ref)
+    print(f"down B={B} {path}: err {e:.3e}")
+    assert e <= TOL
