@@ -11,6 +11,8 @@ synthetic input for the chosen workload:
       the same matrix;
   single_layer_2048       -- 2-bit GEMV 2048x2048, batch 1, no anchors;
   decode14b_b{1,2,4,8}    -- 2-bit GEMV 13824x5120 with 179 fp16 anchors;
+  down70b_b{1,8}          -- 2-bit GEMV 8192x28672 with 1003 fp16 anchors (a
+      70B-shaped down projection); batch 8 runs as K parts;
   decode32b_stack         -- one token through the 448 projection GEMVs of a
       64-layer 32B-shaped decoder (q/k/v and gate/up grouped per launch);
   decode32b_stack_fused   -- the same token as one persistent launch with a
@@ -207,14 +209,16 @@ class SingleLayer2048(Workload):
 
 class Decode14b(Workload):
     N, K = 13824, 5120
+    SEED, PREFIX = 3, "decode14b"
+    ORACLE_ROWS = None  # rows the CPU baseline computes (None: all)
 
     def __init__(self, B):
         import torch
         from bit_weight_quantized_qw_amd import inputs, qw
         self.qw, self.B = qw, B
-        self.name = f"decode14b_b{B}"
-        self.Wh = inputs.weight(self.N, self.K, workload=3)
-        Xp = inputs.profile(256, self.K, workload=3)
+        self.name = f"{self.PREFIX}_b{B}"
+        self.Wh = inputs.weight(self.N, self.K, workload=self.SEED)
+        Xp = inputs.profile(256, self.K, workload=self.SEED)
         self.Xp = Xp
         Wd = torch.from_numpy(self.Wh).cuda()
         idx = qw.qw_select_outliers(Wd, torch.from_numpy(Xp).cuda(), 0.035)
@@ -223,7 +227,7 @@ class Decode14b(Workload):
         del Wd
         self.R = max(2, math.ceil(ROTATE_BYTES / p.nbytes()))
         self.p = _copies(p, self.R)
-        self.xh = inputs.act_f16(B, self.K, workload=3)
+        self.xh = inputs.act_f16(B, self.K, workload=self.SEED)
         self.x = torch.from_numpy(self.xh.view(np.int16)).cuda().view(torch.float16)
         self.y = torch.empty((B, self.N), dtype=torch.float16, device="cuda")
 
@@ -243,11 +247,23 @@ class Decode14b(Workload):
 
     def cpu_baseline(self):
         import oracle
-        r = oracle.quantize_2bit(self.Wh, oracle.select_outliers(self.Wh, self.Xp, 0.035))
+        idx = oracle.select_outliers(self.Wh, self.Xp, 0.035)
+        rows = self.ORACLE_ROWS or self.N
+        r = oracle.quantize_2bit(self.Wh[:rows], idx)
         c2 = oracle.pack_2bit(r["q"])
+        what = "full" if rows == self.N else f"first {rows} rows of"
         return _time_oracle(
             lambda: oracle.gemv_2bit_ref(self.xh, oracle.unpack_2bit(c2), r["S"], r["Z"], r["idx"], r["W_O"]),
-            self.step_amount(), f"full 13824x5120 steps, batch {self.B}")
+            _gemv2_bytes(rows, self.K, self.n_out, self.B), f"{what} {self.N}x{self.K} steps, batch {self.B}")
+
+
+class Down70b(Decode14b):
+    """The down projection of a 70B-shaped decoder (8192 x 28672, 3.5%
+    anchors): at batch 8 its x does not fit one workgroup whole, so the call
+    runs as K parts (grouped launches plus the in-order reduction)."""
+    N, K = 8192, 28672
+    SEED, PREFIX = 6, "down70b"
+    ORACLE_ROWS = 512
 
 
 class Decode32bStack(Workload):
@@ -568,6 +584,7 @@ WORKLOADS = {
     "single_layer_2048": SingleLayer2048,
     "decode14b_b1": lambda: Decode14b(1), "decode14b_b2": lambda: Decode14b(2),
     "decode14b_b4": lambda: Decode14b(4), "decode14b_b8": lambda: Decode14b(8),
+    "down70b_b1": lambda: Down70b(1), "down70b_b8": lambda: Down70b(8),
     "decode32b_stack": Decode32bStack,
     "decode32b_stack_fused": Decode32bStackFused,
     "prefill70b_nf4": lambda: Prefill70b(2), "prefill70b_2bit": lambda: Prefill70b(1),

@@ -957,15 +957,15 @@ int choose_split(const qw_weight &w, const uint16_t *x, int B, int cus) {
   return first;
 }
 
-// Workspace of the K split: one buffer per (device, stream), grown on demand
-// and kept until the process ends. Work on one stream runs in order, so its
-// calls can share the buffer; a replaced buffer is kept too, since a graph
-// captured earlier may still hold its address. Growth calls hipMalloc, so it
-// is refused while the stream is being captured (an eager call of the same
-// shape before the capture sizes the buffer).
+// Workspace of the K split: one buffer per device, grown on demand and kept
+// until the process ends (a replaced buffer is kept too, since a graph
+// captured earlier may still hold its address). Calls on one stream run in
+// order; split calls that overlap on different streams of a device race on
+// it. Growth calls hipMalloc, so it is refused while the stream is being
+// captured (INVALID_ARG, never a silent change of path): an eager call of
+// the same shape before the capture sizes the buffer.
 struct SplitWs {
   int dev;
-  hipStream_t s;
   void *p;
   size_t bytes;
 };
@@ -979,14 +979,14 @@ qw_status split_workspace(hipStream_t s, size_t bytes, float **out) {
   std::lock_guard<std::mutex> lock(g_ws_mu);
   SplitWs *e = nullptr;
   for (auto &w : g_ws)
-    if (w.dev == dev && w.s == s) e = &w;
+    if (w.dev == dev) e = &w;
   if (e && e->bytes >= bytes) {
     *out = reinterpret_cast<float *>(e->p);
     return QW_OK;
   }
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   QW_HIP_TRY(hipStreamIsCapturing(s, &cs));
-  if (cs != hipStreamCaptureStatusNone) return QW_ERR_UNSUPPORTED;
+  if (cs != hipStreamCaptureStatusNone) return QW_ERR_INVALID_ARG;
   const size_t grow = e ? max(bytes, 2 * e->bytes) : max(bytes, (size_t)1 << 20);
   void *p = nullptr;
   QW_HIP_TRY(hipMalloc(&p, grow));
@@ -995,7 +995,7 @@ qw_status split_workspace(hipStream_t s, size_t bytes, float **out) {
     e->p = p;
     e->bytes = grow;
   } else {
-    g_ws.push_back(SplitWs{dev, s, p, grow});
+    g_ws.push_back(SplitWs{dev, p, grow});
   }
   *out = reinterpret_cast<float *>(p);
   return QW_OK;

@@ -329,12 +329,25 @@ def _dt(torch_dtype):
     return m[torch_dtype]
 
 
+def _io_shapes(pw, x, outs):
+    """x must be (B, K) of the weight's K and every output (B, N_i) contiguous
+    on the device: the library reads and writes exactly those sizes."""
+    if x.shape[1] != pw.K:
+        raise ValueError(f"x has {x.shape[1]} columns, the weight K = {pw.K}")
+    for y, N in outs:
+        if not isinstance(y, __import__("torch").Tensor) or not y.is_cuda or not y.is_contiguous():
+            raise ValueError("outputs must be contiguous CUDA tensors")
+        if tuple(y.shape) != (x.shape[0], N):
+            raise ValueError(f"output shape {tuple(y.shape)}, expected {(x.shape[0], N)}")
+
+
 def qgemv_2bit(pw, x, out_dtype=None, out=None):
     import torch
     _need(x, torch.float16, "x", 2)
     out_dtype = out_dtype or torch.float16
     B = x.shape[0]
     y = out if out is not None else torch.empty((B, pw.N), dtype=out_dtype, device=x.device)
+    _io_shapes(pw, x, [(y, pw.N)])
     v = pw.view()
     _check(lib().qgemv_2bit(ctypes.byref(v), _ptr(x), B, _ptr(y), _dt(y.dtype), _stream()),
            "qgemv_2bit")
@@ -347,6 +360,7 @@ def qgemv_nf4(pw, x, out_dtype=None, out=None):
     out_dtype = out_dtype or torch.float16
     B = x.shape[0]
     y = out if out is not None else torch.empty((B, pw.N), dtype=out_dtype, device=x.device)
+    _io_shapes(pw, x, [(y, pw.N)])
     v = pw.view()
     _check(lib().qgemv_nf4(ctypes.byref(v), _ptr(x), B, _ptr(y), _dt(y.dtype), _stream()),
            "qgemv_nf4")
@@ -361,6 +375,10 @@ def qgemv_2bit_grouped(pws, x, out_dtype=None, outs=None):
     n = len(pws)
     ys = outs if outs is not None else [
         torch.empty((B, p.N), dtype=out_dtype, device=x.device) for p in pws]
+    if len(ys) != n:
+        raise ValueError("one output per weight")
+    for p, y in zip(pws, ys):
+        _io_shapes(p, x, [(y, p.N)])
     arr = (qw_weight * n)(*[p.view() for p in pws])
     yp = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
     _check(lib().qgemv_2bit_grouped(arr, n, _ptr(x), B, yp, _dt(ys[0].dtype), _stream()),
@@ -374,6 +392,7 @@ def qgemm_prefill(pw, X, out_dtype=None, out=None):
     out_dtype = out_dtype or torch.bfloat16
     M = X.shape[0]
     Y = out if out is not None else torch.empty((M, pw.N), dtype=out_dtype, device=X.device)
+    _io_shapes(pw, X, [(Y, pw.N)])
     v = pw.view()
     _check(lib().qgemm_prefill(ctypes.byref(v), _ptr(X), M, _ptr(Y), _dt(Y.dtype), _stream()),
            "qgemm_prefill")

@@ -237,13 +237,13 @@ qw_status qw_select_outliers_ex(const void *W, qw_dtype w_dtype, int N, int K,
  * Batches whose x does not fit one workgroup whole (e.g. B >= 2 at
  * K = 27648) run with K cut into equal parts whose fp32 partial rows are
  * added in order; the partials live in a library-owned workspace, one per
- * (device, stream), kept until the process ends and grown with hipMalloc
- * when a larger call comes (B * N * parts * 4 bytes, parts <= 8). Growth is
- * refused with UNSUPPORTED while the stream is being captured into a graph:
- * run the same shape once before capturing. Graphs replay on the stream they
- * were captured from (the workspace is that stream's).
- * Errors: INVALID_ARG (format mismatch, B, dtype), ALIGNMENT, UNSUPPORTED,
- * HIP. */
+ * device, kept until the process ends and grown with hipMalloc when a larger
+ * call comes (B * N * parts * 4 bytes, parts <= 8). Such calls that overlap
+ * on different streams of one device race on it: order them. Growth while
+ * the stream is being captured into a graph is refused with INVALID_ARG:
+ * run the same shape once eagerly before capturing.
+ * Errors: INVALID_ARG (format mismatch, B, dtype, workspace growth during
+ * capture), ALIGNMENT, UNSUPPORTED, HIP. */
 qw_status qgemv_2bit(const qw_weight *w, const void *x, int B, void *y,
                      qw_dtype y_dtype, void *stream);
 

@@ -127,3 +127,48 @@ def test_down_projection_batches(down, B, path, monkeypatch):
     e = norm_err(y[:, rows], ref)
     print(f"down B={B} {path}: err {e:.3e}")
     assert e <= TOL
+
+
+def test_split_call_in_graph_replays_equal_eager(down):
+    """A K-split call captured in a HIP graph (after an eager call of the same
+    shape sized the workspace) replays with the eager call's bits, for new
+    inputs copied in between replays and with other work between them."""
+    import torch
+    pw, _, _ = down
+    B = 8
+    xs = [f16_dev(inputs.act_f16(B, 27648, workload=4, layer=0, proj=20 + i)) for i in range(3)]
+    eager = [qw.qgemv_2bit(pw, xi, out_dtype=torch.float32).clone() for xi in xs]
+    x = torch.empty_like(xs[0])
+    y = torch.zeros((B, 5120), dtype=torch.float32, device="cuda")
+    x.copy_(xs[0])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        qw.qgemv_2bit(pw, x, out=y)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qw.qgemv_2bit(pw, x, out=y)
+    for rep in range(2):
+        for i, xi in enumerate(xs):
+            x.copy_(xi)
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y, eager[i]), (rep, i)
+            float((xi.float() * 2).sum())
+
+
+def test_binding_rejects_mismatched_shapes():
+    """The library reads B x K of x and writes B x N of y: the binding refuses
+    tensors of other shapes before any launch."""
+    import torch
+    W = inputs.weight(64, 1024, workload=93)
+    pw = _packed(W, None)
+    x = torch.zeros((2, 1024), dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError):
+        qw.qgemv_2bit(pw, torch.zeros((2, 512), dtype=torch.float16, device="cuda"))
+    with pytest.raises(ValueError):
+        qw.qgemv_2bit(pw, x, out=torch.zeros((1, 64), dtype=torch.float16, device="cuda"))
+    with pytest.raises(ValueError):
+        qw.qgemv_2bit_grouped([pw, pw], x, outs=[torch.zeros((2, 64), dtype=torch.float16, device="cuda")])
