@@ -36,7 +36,9 @@
  * Conventions for every entry point:
  *  - pointers documented "device" must point to device memory of the
  *    current HIP device; "host" pointers to host memory. The caller owns
- *    and frees all memory; nothing is retained after the call returns.
+ *    and frees all memory it passes; nothing of it is retained after the
+ *    call returns. The one library-owned buffer is the K-split workspace of
+ *    qgemv_2bit (one per device, kept until the process ends).
  *  - ``stream`` is a hipStream_t passed as void* (NULL = default stream).
  *    Device work is only enqueued; no entry point synchronizes.
  *  - arguments are validated on the host before anything is enqueued; on
