@@ -264,7 +264,13 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
          QW_SEL(abase)};
 #undef QW_SEL
   const int K = a.K;
-  const int ldk = a.ldk;
+  // The raw-x variant serves unsplit launches only (the host never pairs it
+  // with K parts), so there the part fields are constants: rows of K
+  // channels and n_out_pad anchors, no part offsets.
+  const int ldk = XR ? K : a.ldk;
+  const int kbase = XR ? 0 : M.kbase;
+  const int abase = XR ? 0 : M.abase;
+  const int ld_a = XR ? M.n_out_pad : M.ld_a;
   const int G = K >> 5;
   const int SC = K >> 9;
   const int wi = bid - M.wg_begin;
@@ -294,12 +300,12 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
   // ---- per-lane load offsets ----
   const uint32_t rb_c = (uint32_t)ldk / 4;         // code bytes per row
   const uint32_t rb_s = (uint32_t)ldk / 8;         // S/Z bytes per row
-  const uint32_t rb_a = (uint32_t)M.ld_a * 2;      // anchor bytes per row
+  const uint32_t rb_a = (uint32_t)ld_a * 2;        // anchor bytes per row
   const uint32_t lim_a = (uint32_t)M.n_out_pad * 2; // this part's anchor bytes per row
   // sizes from the part's first channel (anchor) to the end of the matrix
-  const uint32_t n_codes = (uint32_t)((size_t)M.N * rb_c - (uint32_t)M.kbase / 4);
-  const uint32_t n_sz = (uint32_t)((size_t)M.N * rb_s - (uint32_t)M.kbase / 8);
-  const uint32_t n_wo = (uint32_t)((size_t)M.N * rb_a - (uint32_t)M.abase * 2);
+  const uint32_t n_codes = (uint32_t)((size_t)M.N * rb_c - (uint32_t)kbase / 4);
+  const uint32_t n_sz = (uint32_t)((size_t)M.N * rb_s - (uint32_t)kbase / 8);
+  const uint32_t n_wo = (uint32_t)((size_t)M.N * rb_a - (uint32_t)abase * 2);
 
   // ring slot = three 16-byte loads per lane. Code step: lane (row j,
   // slot g) takes groups 16 sc + 4g .. +3 of its row: codes bytes [32g, 32g+32)
@@ -363,7 +369,7 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
 #pragma unroll
       for (int t = 1; t < B; ++t) b += bg >= t * G;
       const int gr = bg - b * G;
-      const uint32_t xoff = ok ? (uint32_t)((b * ldk + M.kbase + gr * 32 + qt * 8) * 2) : kOob;
+      const uint32_t xoff = ok ? (uint32_t)((b * ldk + kbase + gr * 32 + qt * 8) * 2) : kOob;
       xv[q] = XC ? ld4_coherent(r_x, xoff, 0) : ld4(r_x, xoff, 0);
       if (has_mask) mk[q] = ld1(r_mask, ok ? (uint32_t)gr * 4 : kOob, 0);
     }
