@@ -172,3 +172,35 @@ def test_binding_rejects_mismatched_shapes():
         qw.qgemv_2bit(pw, x, out=torch.zeros((1, 64), dtype=torch.float16, device="cuda"))
     with pytest.raises(ValueError):
         qw.qgemv_2bit_grouped([pw, pw], x, outs=[torch.zeros((2, 64), dtype=torch.float16, device="cuda")])
+
+
+def test_grouped_call_of_split_matrices_equals_separate_calls():
+    """Matrices that run as K parts (batch 2 at K = 27648) in one grouped
+    call: each is launched alone, so the outputs equal separate calls."""
+    import torch
+    K = 27648
+    pws = []
+    for p, N in enumerate((100, 40)):
+        W = inputs.weight(N, K, workload=94, proj=p)
+        pws.append(_packed(W, _anchors(K, 300, 94 + p)))
+    x = f16_dev(inputs.act_f16(2, K, workload=94))
+    ys = qw.qgemv_2bit_grouped(pws, x, out_dtype=torch.float32)
+    for pw, yg in zip(pws, ys):
+        ysep = qw.qgemv_2bit(pw, x, out_dtype=torch.float32)
+        np.testing.assert_array_equal(yg.cpu().numpy(), ysep.cpu().numpy())
+
+
+@pytest.mark.parametrize("forced", ["5", "9", "1"])
+def test_invalid_forced_part_count_falls_back(forced, monkeypatch):
+    """A forced part count that does not divide the super-chunks or does not
+    fit (or 1 where the batch cannot run whole) leaves the automatic choice,
+    bit for bit."""
+    import torch
+    N, K = 64, 27648
+    W = inputs.weight(N, K, workload=95)
+    pw = _packed(W, _anchors(K, 500, 95))
+    x = f16_dev(inputs.act_f16(4, K, workload=95))
+    auto = qw.qgemv_2bit(pw, x, out_dtype=torch.float32).cpu().numpy()
+    monkeypatch.setenv("QW_GEMV_SPLIT", forced)
+    got = qw.qgemv_2bit(pw, x, out_dtype=torch.float32).cpu().numpy()
+    np.testing.assert_array_equal(got, auto)
