@@ -951,11 +951,15 @@ int choose_split(const qw_weight &w, const uint16_t *x, int B, int cus) {
   int first = 0;
   for (int ks = 2; ks <= kMaxSplit; ++ks) {
     if (SC % ks != 0) continue;
-    Args ap;
-    int gp = 0;
-    if (plan_part(w, ks, 0, x, cus, ap, gp) != QW_OK) continue;
-    // part 0 holds the longest anchor run
-    if (!fits_one_wg(B, ap.K, ap.xo_len, ap.units_max, 0)) continue;
+    // every part must fit (their anchor runs differ by up to one chunk)
+    bool fit = true;
+    for (int p = 0; p < ks && fit; ++p) {
+      Args ap;
+      int gp = 0;
+      fit = plan_part(w, ks, p, x, cus, ap, gp) == QW_OK &&
+            fits_one_wg(B, ap.K, ap.xo_len, ap.units_max, 0);
+    }
+    if (!fit) continue;
     if (forced == ks) return ks;
     if (first == 0) first = ks;
   }
@@ -1018,7 +1022,7 @@ bool deep_ring() {
 qw_status launch_split(const qw_weight &w, int ks, const uint16_t *x, int B, void *y, bool f32, int cus,
                        hipStream_t s) {
   const size_t plane = (size_t)B * w.N;
-  if (plane >= (1u << 31) / 2) return QW_ERR_UNSUPPORTED;
+  if (plane > (size_t)INT32_MAX) return QW_ERR_UNSUPPORTED;  // int indices in the reduction
   Args parts_a[kMaxSplit];
   int grid_p = 0;
   for (int p = 0; p < ks; ++p) QW_TRY(plan_part(w, ks, p, x, cus, parts_a[p], grid_p));
