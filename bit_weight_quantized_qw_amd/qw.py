@@ -332,10 +332,11 @@ def _dt(torch_dtype):
 def _io_shapes(pw, x, outs):
     """x must be (B, K) of the weight's K and every output (B, N_i) contiguous
     on the device: the library reads and writes exactly those sizes."""
+    import torch
     if x.shape[1] != pw.K:
         raise ValueError(f"x has {x.shape[1]} columns, the weight K = {pw.K}")
     for y, N in outs:
-        if not isinstance(y, __import__("torch").Tensor) or not y.is_cuda or not y.is_contiguous():
+        if not isinstance(y, torch.Tensor) or not y.is_cuda or not y.is_contiguous():
             raise ValueError("outputs must be contiguous CUDA tensors")
         if tuple(y.shape) != (x.shape[0], N):
             raise ValueError(f"output shape {tuple(y.shape)}, expected {(x.shape[0], N)}")
