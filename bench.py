@@ -6,15 +6,20 @@
 Prints ONE JSON line. A step is one pass of the hot path over one batch of
 synthetic input for the chosen workload:
 
-  llama7b_mlp_up_gemv (default) -- W 11008x4096 N(0, 0.02^2), batch-1 fp16
+  decode32b_stack (default) -- one token through the 448 projection GEMVs of
+      a 64-layer 32B-shaped decoder (q/k/v and gate/up grouped per launch),
+      2-bit G32 with 3.5% fp16 anchors, 13.9 GB of weights per token. The
+      line also carries a ``prefill`` object: the 70B-shaped 2-bit prefill
+      GEMM (2048x8192 bf16 times 28672x8192) timed in the same run, so both
+      halves of the metric (GEMV GB/s, prefill TFLOP/s) come from one run;
+  llama7b_mlp_up_gemv     -- W 11008x4096 N(0, 0.02^2), batch-1 fp16
       activations; one NF4 (block 64) GEMV and one 2-bit (group 32) GEMV of
       the same matrix;
   single_layer_2048       -- 2-bit GEMV 2048x2048, batch 1, no anchors;
   decode14b_b{1,2,4,8}    -- 2-bit GEMV 13824x5120 with 179 fp16 anchors;
   down70b_b{1,8}          -- 2-bit GEMV 8192x28672 with 1003 fp16 anchors (a
-      70B-shaped down projection); batch 8 runs as K parts;
-  decode32b_stack         -- one token through the 448 projection GEMVs of a
-      64-layer 32B-shaped decoder (q/k/v and gate/up grouped per launch);
+      70B-shaped down projection); batch 8 runs as K parts (qgemv_2bit_ws
+      with a caller-owned workspace);
   decode32b_stack_fused   -- the same token as one persistent launch with a
       device-wide barrier between its 256 stages;
   prefill70b_nf4 / prefill70b_2bit -- 2048x8192 bf16 times 28672x8192;
@@ -70,6 +75,7 @@ def log(*a):
 class Workload:
     """launches(i): list of (kernel_name, callable) making up step i."""
     name = ""
+    steps, warmup = 200, 20  # defaults when the command line gives none
     library = True  # every launch is one libqw entry-point call
     # whole-step time from replays of steps captured in a HIP graph (the
     # per-launch kernel times still come from the eager pass)
@@ -230,10 +236,12 @@ class Decode14b(Workload):
         self.xh = inputs.act_f16(B, self.K, workload=self.SEED)
         self.x = torch.from_numpy(self.xh.view(np.int16)).cuda().view(torch.float16)
         self.y = torch.empty((B, self.N), dtype=torch.float16, device="cuda")
+        # caller-owned K-split workspace (None where the batch runs whole)
+        self.ws = qw.gemv_workspace(self.p[0], B)
 
     def launches(self, i):
         r = i % self.R
-        return [("qgemv_2bit", lambda: self.qw.qgemv_2bit(self.p[r], self.x, out=self.y))]
+        return [("qgemv_2bit", lambda: self.qw.qgemv_2bit_ws(self.p[r], self.x, self.ws, out=self.y))]
 
     def kernel_amount(self):
         return {"qgemv_2bit": _gemv2_bytes(self.N, self.K, self.n_out, self.B)}
@@ -270,6 +278,7 @@ class Decode32bStack(Workload):
     """64 layers x {qkv (grouped), o, gate+up (grouped), down}, batch 1.
     One token is 256 launches against distinct per-layer weights."""
     name = "decode32b_stack"
+    steps, warmup = 50, 5
     L, H, I, KV = 64, 5120, 27648, 1024
     PROJ = [("q", 5120, 5120, 0), ("k", 1024, 5120, 0), ("v", 1024, 5120, 0),
             ("o", 5120, 5120, 1), ("gate", 27648, 5120, 2), ("up", 27648, 5120, 2),
@@ -404,6 +413,7 @@ class Decode32bStackFused(Decode32bStack):
 
 
 class Prefill70b(Workload):
+    steps, warmup = 40, 5
     M, N, K = 2048, 28672, 8192
     unit = "TFLOP/s"
     bound = "mfma"
@@ -466,8 +476,9 @@ class PrepLlama7b(Workload):
     """Device-side weight preparation of one 11008x4096 projection from fp16
     weights: profile sums, anchor selection, refined 2-bit pack."""
     name = "prep_llama7b_refine5"
+    steps, warmup = 20, 3
     N, K, P, ROUNDS = 11008, 4096, 256, 5
-    graph = False  # the selection allocates stream-ordered scratch
+    graph = False  # a preparation step, timed as issued once per weight
     bound = "alu"
     dtype = "f64"
 
@@ -707,10 +718,12 @@ def run_graph(wl, steps, max_nodes=2048):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="llama7b_mlp_up_gemv", choices=sorted(WORKLOADS))
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: per workload)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default: per workload)")
+    ap.add_argument("--workload", default="decode32b_stack", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="leave out the prefill object of the default workload's line")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -727,9 +740,32 @@ def main():
 
     wl = WORKLOADS[args.workload]()
     log(f"workload {wl.name}: setup done")
+    steps = args.steps if args.steps is not None else wl.steps
+    warmup = args.warmup if args.warmup is not None else wl.warmup
     torch.cuda.synchronize()
-    total_ms, per_kernel, wall_ms = run(wl, args.steps, args.warmup)
-    ms_per_step = total_ms / args.steps
+    out = measure(wl, steps, warmup, args.traffic_json)
+    log(f"workload {wl.name}: {out['ms_per_step']} ms per step")
+    if wl.name == "decode32b_stack" and not args.no_prefill:
+        # the other half of the metric, timed in the same run
+        pf = Prefill70b(1)
+        log(f"workload {pf.name}: setup done")
+        torch.cuda.synchronize()
+        p = measure(pf, pf.steps, pf.warmup, args.traffic_json)
+        out["prefill"] = {k: p[k] for k in ("value", "unit", "steps", "warmup", "ms_per_step", "dtype",
+                                           "config", "roofline", "kernels", "step_timing")}
+        log(f"workload {pf.name}: {p['ms_per_step']} ms per call")
+    if not args.no_cpu_baseline:
+        cb = wl.cpu_baseline()
+        if cb is not None:
+            cb["unit"] = wl.unit
+            out["cpu_baseline"] = cb
+    print(json.dumps(out), flush=True)
+
+
+def measure(wl, steps, warmup, traffic_json):
+    """Times one workload; returns the fields of the JSON line."""
+    total_ms, per_kernel, wall_ms = run(wl, steps, warmup)
+    ms_per_step = total_ms / steps
     scale = 1e12 if wl.unit == "TFLOP/s" else 1e9
     value = wl.step_amount() / (ms_per_step * 1e-3) / scale
 
@@ -747,11 +783,11 @@ def main():
         peak, roof_unit = FP64_PEAK_TFLOPS, "TFLOP/s"
         avg_s = kstats[dominant]["avg_us"] * 1e-6
         ach = round(wl.roof_amount()[dominant] / avg_s / 1e12, 3)
-    traffic = _traffic(args.traffic_json, wl.name, dominant)
+    traffic = _traffic(traffic_json, wl.name, dominant)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": wl.unit, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": wl.dtype, "data": "synthetic (seeded N(0,0.02^2) weights, N(0,1) activations)",
         "config": wl.config(),
@@ -766,12 +802,7 @@ def main():
         out["tokens_per_s"] = round(1e3 / ms_per_step, 2)
     if hasattr(wl, "stack"):
         out["barrier_timeouts"] = wl.stack.error()
-    if not args.no_cpu_baseline:
-        cb = wl.cpu_baseline()
-        if cb is not None:
-            cb["unit"] = wl.unit
-            out["cpu_baseline"] = cb
-    print(json.dumps(out), flush=True)
+    return out
 
 
 if __name__ == "__main__":

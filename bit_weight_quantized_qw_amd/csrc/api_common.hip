@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include <hip/hip_ext.h>
@@ -70,6 +71,15 @@ void build_nf4() {
   for (int i = 0; i < 16; ++i) g_nf4[i] = (float)(v[i] / mx);
 }
 }  // namespace
+
+// Test hooks (qw_tuning.h), indexed by key; -1 = automatic.
+constexpr int kTuneKeys = 6;
+std::atomic<int> g_tune[kTuneKeys] = {{-1}, {-1}, {-1}, {-1}, {-1}, {-1}};
+
+int tune(qw_tune_key key) {
+  const int k = (int)key;
+  return (k > 0 && k < kTuneKeys) ? g_tune[k].load(std::memory_order_relaxed) : QW_TUNE_AUTO;
+}
 
 const float *nf4_levels_host() {
   std::call_once(g_nf4_once, build_nf4);
@@ -158,6 +168,19 @@ qw_status qw_time_next_call(void *start_event, void *stop_event) {
 }
 
 int qw_abi_version(void) { return QW_ABI_VERSION; }
+
+qw_status qw_tune_set(qw_tune_key key, int value) {
+  const int k = (int)key;
+  if (k <= 0 || k >= qw::kTuneKeys || value < QW_TUNE_AUTO) return QW_ERR_INVALID_ARG;
+  qw::g_tune[k].store(value, std::memory_order_relaxed);
+  return QW_OK;
+}
+
+int qw_tune_get(qw_tune_key key) { return qw::tune(key); }
+
+size_t qw_select_workspace_bytes(int K) {
+  return K > 0 ? (size_t)K * (2 * sizeof(double) + sizeof(int32_t)) : 0;
+}
 
 const char *qw_status_str(qw_status s) {
   switch (s) {

@@ -1,24 +1,18 @@
 // Host side of the 2-bit decode GEMV: validation, work split, dispatch.
 // The kernel itself (and the decode scheme) is in gemv2_kernel.h.
-#include <stdlib.h>
-
 #include "gemv2_kernel.h"
 
 namespace qw {
 namespace gemv2m {
 qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void *const *ys,
-                 bool f32, int cus, hipStream_t s);
+                 bool f32, int cus, float *work, size_t work_bytes, hipStream_t s);
+size_t split_workspace_bytes(const qw_weight &w, int B, int cus);
 }  // namespace gemv2m
 
 namespace gemv2 {
 namespace {
 
 int max_uw(int B) { return B == 1 ? 8 : (B == 2 ? 3 : 2); }
-
-int env_int(const char *name, int dflt) {
-  const char *v = getenv(name);
-  return v ? atoi(v) : dflt;
-}
 
 // Launch geometry for one batch slice of width Bk.
 struct Plan {
@@ -46,9 +40,9 @@ bool plan_slice(const qw_weight *ws, int count, int Bk, int cus, Plan *p, int *r
   const int UA = ua_need == 0 ? 0 : (ua_need <= 2 ? 2 : 4);
   const int V = kMaxWaves / W;
   const int threads = 64 * W * V;
-  const long target_wgs = max(1L, (long)cus * env_int("QW_GEMV_WG_PER_CU", 1));
-  int rpg = env_int("QW_GEMV_ROWS_PER_WG", 0);
-  if (rpg <= 0) rpg = (int)max(1L, (total_rows + target_wgs - 1) / target_wgs);
+  // one workgroup per CU
+  const long target_wgs = max(1L, (long)cus);
+  const int rpg = (int)max(1L, (total_rows + target_wgs - 1) / target_wgs);
   int grid = 0;
   for (int i = 0; i < count; ++i) {
     wg_begin_out[i] = grid;
@@ -99,27 +93,37 @@ qw_status launch_slice(const qw_weight *ws, int count, const uint16_t *x, int Bk
 qw_status launch_valu(const qw_weight *ws, int count, const uint16_t *x, int B, void *const *ys,
                       bool f32, int cus, hipStream_t s);
 
-qw_status launch(const qw_weight *ws, int count, const void *x, int B, void *const *ys,
-                 qw_dtype dt, hipStream_t s) {
-  if (!ws || count < 1 || count > kMaxMats || !x || !ys) return QW_ERR_INVALID_ARG;
+// Argument checks shared by the entry points (and the workspace query).
+qw_status check_args(const qw_weight *ws, int count, int B) {
+  if (!ws || count < 1 || count > kMaxMats) return QW_ERR_INVALID_ARG;
   if (B < 1 || B > 8) return QW_ERR_INVALID_ARG;
-  if (dt != QW_DT_F16 && dt != QW_DT_F32) return QW_ERR_INVALID_ARG;
   const int K = ws[0].K;
   for (int i = 0; i < count; ++i) {
     qw_status st = check_weight_view(&ws[i], QW_FMT_2BIT_G32, K);
     if (st != QW_OK) return st;
-    if (!ys[i]) return QW_ERR_INVALID_ARG;
-    if (!aligned16(ys[i])) return QW_ERR_ALIGNMENT;
-  }
-  if (!aligned16(x)) return QW_ERR_ALIGNMENT;
-  int cus = 0;
-  qw_status st = current_device(&cus);
-  if (st != QW_OK) return st;
-  const bool f32 = dt == QW_DT_F32;
-  for (int i = 0; i < count; ++i) {
     // buffer offsets are 32-bit
     if ((size_t)ws[i].N * (ws[i].K / 4) >= (1ull << 31)) return QW_ERR_UNSUPPORTED;
   }
+  return QW_OK;
+}
+
+// work / work_bytes: the caller's K-split workspace (NULL / 0: none).
+qw_status launch(const qw_weight *ws, int count, const void *x, int B, void *const *ys,
+                 qw_dtype dt, void *work, size_t work_bytes, hipStream_t s) {
+  QW_TRY(check_args(ws, count, B));
+  if (!x || !ys) return QW_ERR_INVALID_ARG;
+  if (dt != QW_DT_F16 && dt != QW_DT_F32) return QW_ERR_INVALID_ARG;
+  if (work_bytes > 0 && !work) return QW_ERR_INVALID_ARG;
+  for (int i = 0; i < count; ++i) {
+    if (!ys[i]) return QW_ERR_INVALID_ARG;
+    if (!aligned16(ys[i])) return QW_ERR_ALIGNMENT;
+  }
+  if (!aligned16(x) || !aligned16(work)) return QW_ERR_ALIGNMENT;
+  int cus = 0;
+  qw_status st = current_device(&cus);
+  if (st != QW_OK) return st;
+  const int K = ws[0].K;
+  const bool f32 = dt == QW_DT_F32;
   // the matrix-core kernel takes the whole batch in one pass when the shape
   // fits it; otherwise batch rows go through vector-ALU kernels of width 4,
   // 2 and 1 (e.g. 7 = 4 + 2 + 1).
@@ -128,13 +132,13 @@ qw_status launch(const qw_weight *ws, int count, const void *x, int B, void *con
   // matrices whose 16-row tiles spread evenly over the CUs (at least 3/4 of
   // the slots of the busiest round filled: 4096 or 8192 rows on 256 CUs),
   // the vector-ALU kernel (which splits rows, not tiles) otherwise (5120
-  // rows: 320 tiles). QW_GEMV_VALU=1 forces the vector-ALU kernel and
-  // QW_GEMV_VALU=0 the matrix-core one where it applies (for tests).
+  // rows: 320 tiles). The test hook QW_TUNE_GEMV2_PATH = 1 forces the
+  // vector-ALU kernel and 0 the matrix-core one where it applies.
   // The choice is made per matrix (a grouped call gives the bits of
   // separate calls): the matrices that take the matrix-core kernel go out as
   // one grouped launch of it (or one by one when the group does not fit it),
   // the rest as grouped launches of the vector-ALU kernel.
-  const int force = env_int("QW_GEMV_VALU", -1);
+  const int force = tune(QW_TUNE_GEMV2_PATH);
   qw_weight mc_w[kMaxMats], va_w[kMaxMats];
   void *mc_y[kMaxMats], *va_y[kMaxMats];
   int n_mc = 0, n_va = 0;
@@ -153,10 +157,11 @@ qw_status launch(const qw_weight *ws, int count, const void *x, int B, void *con
   }
   const uint16_t *xh = reinterpret_cast<const uint16_t *>(x);
   if (n_mc > 0) {
-    st = gemv2m::launch(mc_w, n_mc, xh, B, mc_y, f32, cus, s);
+    float *wk = reinterpret_cast<float *>(work);
+    st = gemv2m::launch(mc_w, n_mc, xh, B, mc_y, f32, cus, wk, work_bytes, s);
     if (st == QW_ERR_UNSUPPORTED) {
       for (int i = 0; i < n_mc; ++i) {
-        st = gemv2m::launch(&mc_w[i], 1, xh, B, &mc_y[i], f32, cus, s);
+        st = gemv2m::launch(&mc_w[i], 1, xh, B, &mc_y[i], f32, cus, wk, work_bytes, s);
         if (st == QW_ERR_UNSUPPORTED) {
           va_w[n_va] = mc_w[i];
           va_y[n_va++] = mc_y[i];
@@ -209,13 +214,31 @@ qw_status qgemv_2bit(const qw_weight *w, const void *x, int B, void *y, qw_dtype
                      void *stream) {
   qw::CallScope scope;
   void *ys[1] = {y};
-  return qw::gemv2::launch(w, 1, x, B, ys, y_dtype, qw::as_stream(stream));
+  return qw::gemv2::launch(w, 1, x, B, ys, y_dtype, nullptr, 0, qw::as_stream(stream));
+}
+
+qw_status qgemv_2bit_ws(const qw_weight *w, const void *x, int B, void *y, qw_dtype y_dtype,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+  qw::CallScope scope;
+  void *ys[1] = {y};
+  return qw::gemv2::launch(w, 1, x, B, ys, y_dtype, workspace, workspace_bytes, qw::as_stream(stream));
+}
+
+qw_status qgemv_2bit_workspace_bytes(const qw_weight *w, int B, size_t *bytes) {
+  using namespace qw;
+  if (!bytes) return QW_ERR_INVALID_ARG;
+  QW_TRY(gemv2::check_args(w, 1, B));
+  int cus = 0;
+  QW_TRY(current_device(&cus));
+  // the vector-ALU path (forced by the test hook, or K % 512 != 0) needs none
+  *bytes = tune(QW_TUNE_GEMV2_PATH) == 1 ? 0 : gemv2m::split_workspace_bytes(*w, B, cus);
+  return QW_OK;
 }
 
 qw_status qgemv_2bit_grouped(const qw_weight *ws, int count, const void *x, int B,
                              void *const *ys, qw_dtype y_dtype, void *stream) {
   qw::CallScope scope;
-  return qw::gemv2::launch(ws, count, x, B, ys, y_dtype, qw::as_stream(stream));
+  return qw::gemv2::launch(ws, count, x, B, ys, y_dtype, nullptr, 0, qw::as_stream(stream));
 }
 
 }  // extern "C"

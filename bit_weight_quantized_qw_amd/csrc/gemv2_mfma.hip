@@ -807,8 +807,6 @@ static qw_status plan(const qw_weight *ws, int count, const uint16_t *x, void *c
   // every matrix is planned as if it were launched alone (its workgroup
   // count, hence its K split and summation order, do not depend on what it
   // is grouped with), so a grouped launch gives the bits of separate ones
-  const char *wpc = getenv("QW_GEMV_MC_WG_PER_CU");
-  const int wgs_per_cu = wpc ? max(1, atoi(wpc)) : 1;
   int units_max = 0;
   grid = 0;
   for (int i = 0; i < count; ++i) {
@@ -824,7 +822,7 @@ static qw_status plan(const qw_weight *ws, int count, const uint16_t *x, void *c
     m.n_out_pad = ws[i].n_out > 0 ? ws[i].n_out_pad : 0;
     m.ld_a = m.n_out_pad;
     m.tiles = (m.N + 15) / 16;
-    m.wg_count = max(1, min(m.tiles, cus * wgs_per_cu));
+    m.wg_count = max(1, min(m.tiles, cus));
   }
   long want = 0, all_tiles = 0;
   for (int i = 0; i < count; ++i) {
@@ -872,11 +870,6 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *parts, i
 namespace {
 
 constexpr int kMaxSplit = 8;
-
-int env_int(const char *name, int dflt) {
-  const char *v = getenv(name);
-  return v ? atoi(v) : dflt;
-}
 
 bool fits_one_wg(int b, int K, int xo_len, int units_max, int xr) {
   return (long)b * K <= (long)kXItems * kThreads * 8 &&
@@ -934,18 +927,17 @@ qw_status plan_part(const qw_weight &w, int ks, int p, const uint16_t *x, int cu
 // take the shape. Measured on MI355X, a split pays only where no unsplit
 // pass of two or more batch rows fits (the split's extra workgroups each
 // prepare their share of x for the whole batch, and the parts cost one more
-// launch), and there the fewest parts that fit are fastest. QW_GEMV_SPLIT=n
-// forces n parts where n is valid (tests).
-int choose_split(const qw_weight &w, const uint16_t *x, int B, int cus) {
+// launch), and there the fewest parts that fit are fastest. The test hook
+// QW_TUNE_GEMV2_SPLIT = n forces n parts where n is valid.
+int choose_split_uncached(const qw_weight &w, int B, int cus, int forced) {
   const int K = w.K;
   if (K % 512 != 0) return 0;
   Args a;
   int grid = 0;
   void *dummy = nullptr;
-  if (plan(&w, 1, x, &dummy, true, cus, a, grid) != QW_OK) return 0;
+  if (plan(&w, 1, nullptr, &dummy, true, cus, a, grid) != QW_OK) return 0;
   int xr = 1, bmax = 0;
   const int ns = unsplit_slices(a, B, &xr, &bmax);
-  const int forced = env_int("QW_GEMV_SPLIT", 0);
   if (ns > 0 && forced <= 1) return 1;
   const int SC = K / 512;
   int first = 0;
@@ -956,7 +948,7 @@ int choose_split(const qw_weight &w, const uint16_t *x, int B, int cus) {
     for (int p = 0; p < ks && fit; ++p) {
       Args ap;
       int gp = 0;
-      fit = plan_part(w, ks, p, x, cus, ap, gp) == QW_OK &&
+      fit = plan_part(w, ks, p, nullptr, cus, ap, gp) == QW_OK &&
             fits_one_wg(B, ap.K, ap.xo_len, ap.units_max, 0);
     }
     if (!fit) continue;
@@ -967,67 +959,60 @@ int choose_split(const qw_weight &w, const uint16_t *x, int B, int cus) {
   return first;
 }
 
-// Workspace of the K split: one buffer per device, grown on demand and kept
-// until the process ends (a replaced buffer is kept too, since a graph
-// captured earlier may still hold its address). Calls on one stream run in
-// order; split calls that overlap on different streams of a device race on
-// it. Growth calls hipMalloc, so it is refused while the stream is being
-// captured (INVALID_ARG, never a silent change of path): an eager call of
-// the same shape before the capture sizes the buffer.
-struct SplitWs {
-  int dev;
-  void *p;
-  size_t bytes;
+// The choice depends on the shape only, so it is planned once per shape
+// (a small table, replaced round-robin) instead of on every call.
+struct SplitKey {
+  int N, K, n_out, n_out_pad, B, cus, forced;
+  bool operator==(const SplitKey &o) const {
+    return N == o.N && K == o.K && n_out == o.n_out && n_out_pad == o.n_out_pad && B == o.B &&
+           cus == o.cus && forced == o.forced;
+  }
 };
-std::mutex g_ws_mu;
-std::vector<SplitWs> g_ws;
-std::vector<void *> g_ws_retired;
+constexpr int kSplitCache = 64;
+struct SplitCache {
+  std::mutex mu;
+  SplitKey key[kSplitCache];
+  int ks[kSplitCache];
+  int used = 0, next = 0;
+};
+SplitCache g_split;
 
-qw_status split_workspace(hipStream_t s, size_t bytes, float **out) {
-  int dev = 0;
-  QW_HIP_TRY(hipGetDevice(&dev));
-  std::lock_guard<std::mutex> lock(g_ws_mu);
-  SplitWs *e = nullptr;
-  for (auto &w : g_ws)
-    if (w.dev == dev) e = &w;
-  if (e && e->bytes >= bytes) {
-    *out = reinterpret_cast<float *>(e->p);
-    return QW_OK;
+int choose_split(const qw_weight &w, int B, int cus) {
+  const int forced = tune(QW_TUNE_GEMV2_SPLIT);
+  const SplitKey k{w.N, w.K, w.n_out, w.n_out > 0 ? w.n_out_pad : 0, B, cus, forced};
+  {
+    std::lock_guard<std::mutex> lock(g_split.mu);
+    for (int i = 0; i < g_split.used; ++i)
+      if (g_split.key[i] == k) return g_split.ks[i];
   }
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  QW_HIP_TRY(hipStreamIsCapturing(s, &cs));
-  if (cs != hipStreamCaptureStatusNone) return QW_ERR_INVALID_ARG;
-  const size_t grow = e ? max(bytes, 2 * e->bytes) : max(bytes, (size_t)1 << 20);
-  void *p = nullptr;
-  QW_HIP_TRY(hipMalloc(&p, grow));
-  if (e) {
-    g_ws_retired.push_back(e->p);
-    e->p = p;
-    e->bytes = grow;
-  } else {
-    g_ws.push_back(SplitWs{dev, p, grow});
-  }
-  *out = reinterpret_cast<float *>(p);
-  return QW_OK;
+  const int ks = choose_split_uncached(w, B, cus, forced);
+  std::lock_guard<std::mutex> lock(g_split.mu);
+  const int slot = g_split.used < kSplitCache ? g_split.used++ : (g_split.next++ % kSplitCache);
+  g_split.key[slot] = k;
+  g_split.ks[slot] = ks;
+  return ks;
 }
 
 bool deep_ring() {
   // 3 ring slots per wave: measured on MI355X, the deep ring (6 slots up to
   // batch 2, 4 beyond) is slower with weights coming from HBM even for waves
-  // with many steps; QW_GEMV_MC_DEEP=1 selects it (tests check both give the
-  // same bits)
-  return env_int("QW_GEMV_MC_DEEP", 0) != 0;
+  // with many steps; the test hook QW_TUNE_GEMV2_DEEP_RING = 1 selects it
+  // (tests check both give the same bits)
+  return tune(QW_TUNE_GEMV2_DEEP_RING) == 1;
 }
 
+// fp32 partial rows of ks parts at batch B
+size_t split_bytes(const qw_weight &w, int ks, int B) { return (size_t)ks * B * w.N * sizeof(float); }
+
+// The parts write their fp32 partial rows to ``parts`` (the caller's
+// workspace, split_bytes long); the reduction adds them in part order.
 qw_status launch_split(const qw_weight &w, int ks, const uint16_t *x, int B, void *y, bool f32, int cus,
-                       hipStream_t s) {
+                       float *parts, hipStream_t s) {
   const size_t plane = (size_t)B * w.N;
   if (plane > (size_t)INT32_MAX) return QW_ERR_UNSUPPORTED;  // int indices in the reduction
   Args parts_a[kMaxSplit];
   int grid_p = 0;
   for (int p = 0; p < ks; ++p) QW_TRY(plan_part(w, ks, p, x, cus, parts_a[p], grid_p));
-  float *parts = nullptr;
-  QW_TRY(split_workspace(s, (size_t)ks * plane * sizeof(float), &parts));
   const bool deep = deep_ring();
   qw_status st = QW_OK;
   for (int p0 = 0; p0 < ks && st == QW_OK; p0 += kMats) {
@@ -1053,17 +1038,30 @@ qw_status launch_split(const qw_weight &w, int ks, const uint16_t *x, int B, voi
 
 }  // namespace
 
+// Workspace bytes of a K-split call of w at batch B (0: runs unsplit or not
+// on this kernel).
+size_t split_workspace_bytes(const qw_weight &w, int B, int cus) {
+  if (B < 1 || B > 8) return 0;
+  const int ks = choose_split(w, B, cus);
+  return ks > 1 ? split_bytes(w, ks, B) : 0;
+}
+
 // Returns QW_ERR_UNSUPPORTED (nothing enqueued) when the shape does not fit
-// this kernel; the caller then uses the vector-ALU kernel. A grouped call
-// whose matrices would be split alone is refused too (the caller then
-// launches them one by one), so that it gives the bits of separate calls.
+// this kernel, or needs K parts and ``work`` (the caller's workspace of
+// work_bytes) cannot hold their partial rows; the caller then uses the
+// vector-ALU kernel. A grouped call whose matrices would be split alone is
+// refused too (the caller then launches them one by one), so that it gives
+// the bits of separate calls.
 qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void *const *ys,
-                 bool f32, int cus, hipStream_t s) {
+                 bool f32, int cus, float *work, size_t work_bytes, hipStream_t s) {
   if (B < 1 || B > 8) return QW_ERR_UNSUPPORTED;
   for (int i = 0; i < count; ++i) {
-    const int ks = choose_split(ws[i], x, B, cus);
+    const int ks = choose_split(ws[i], B, cus);
     if (ks == 0) return QW_ERR_UNSUPPORTED;
-    if (ks > 1) return count == 1 ? launch_split(ws[0], ks, x, B, ys[0], f32, cus, s) : QW_ERR_UNSUPPORTED;
+    if (ks > 1) {
+      if (count != 1 || !work || work_bytes < split_bytes(ws[0], ks, B)) return QW_ERR_UNSUPPORTED;
+      return launch_split(ws[0], ks, x, B, ys[0], f32, cus, work, s);
+    }
   }
   const int K = ws[0].K;
   Args a;

@@ -322,11 +322,6 @@ qw_status launch_b(const ArgsNf4 &a, int B, int UW, bool deep, int grid, size_t 
   return launch_p<4, 1>(a, deep, grid, lds, s);
 }
 
-int env_int(const char *name, int dflt) {
-  const char *v = getenv(name);
-  return v ? atoi(v) : dflt;
-}
-
 }  // namespace
 }  // namespace qw
 
@@ -360,9 +355,9 @@ extern "C" qw_status qgemv_nf4(const qw_weight *w, const void *x, int B, void *y
       W = 1;
       while (W < 8 && W * 64 * maxuw < NH) W *= 2;
       UW = (NH + 64 * W - 1) / (64 * W);
-      const long target_wgs = max(1L, (long)cus * env_int("QW_GEMV_WG_PER_CU", 1));
-      rpg = env_int("QW_GEMV_ROWS_PER_WG", 0);
-      if (rpg <= 0) rpg = (int)max(1L, ((long)w->N + target_wgs - 1) / target_wgs);
+      // one workgroup per CU
+      const long target_wgs = max(1L, (long)cus);
+      rpg = (int)max(1L, ((long)w->N + target_wgs - 1) / target_wgs);
       grid = (w->N + rpg - 1) / rpg;
       lds = (size_t)Bk * K * 2 + (W > 1 ? 4 * (size_t)rpg * W * Bk : 0);
       if (UW <= maxuw && lds + 256 * kPairStride <= 160 * 1024 && (Bk * (K / 8) + kThreads - 1) / kThreads <= kXLoads) break;
@@ -382,10 +377,10 @@ extern "C" qw_status qgemv_nf4(const qw_weight *w, const void *x, int B, void *y
     const float *lv = nf4_levels_host();
     for (int i = 0; i < 16; ++i) a.L[i] = lv[i];
     // 3 row slots per wave: measured on MI355X, 6 slots (all rows of a wave
-    // in flight at once) are slower with weights coming from HBM;
-    // QW_GEMV_NF4_DEEP=1 selects them (tests check both give the same bits)
-    const char *dv = getenv("QW_GEMV_NF4_DEEP");
-    const bool deep = dv ? atoi(dv) != 0 : false;
+    // in flight at once) are slower with weights coming from HBM; the test
+    // hook QW_TUNE_NF4_DEEP_RING = 1 selects them (tests check both give the
+    // same bits)
+    const bool deep = tune(QW_TUNE_NF4_DEEP_RING) == 1;
     st = launch_b(a, Bk, UW, deep, grid, lds, as_stream(stream));
     if (st != QW_OK) return st;
     b0 += Bk;

@@ -444,7 +444,8 @@ qw_status qw_profile_accumulate(const void *X, qw_dtype x_dtype, int M, int K, d
 }
 
 qw_status qw_select_outliers(const float *W, int N, int K, const float *X_prof, int P,
-                             double frac, qw_score score, int32_t *out_idx, void *stream) {
+                             double frac, qw_score score, int32_t *out_idx, void *workspace,
+                             size_t workspace_bytes, void *stream) {
   using namespace qw;
   CallScope scope;
   if (!W || !X_prof || N <= 0 || K <= 0 || P <= 0) return QW_ERR_INVALID_ARG;
@@ -453,15 +454,15 @@ qw_status qw_select_outliers(const float *W, int N, int K, const float *X_prof, 
   const int n = qw_outlier_count(K, frac);
   if (n < 0) return QW_ERR_INVALID_ARG;
   if (n > 0 && !out_idx) return QW_ERR_INVALID_ARG;
-  if (!aligned16(W) || !aligned16(X_prof) || (n > 0 && !aligned16(out_idx))) return QW_ERR_ALIGNMENT;
+  if (n > 0 && (!workspace || workspace_bytes < qw_select_workspace_bytes(K))) return QW_ERR_INVALID_ARG;
+  if (!aligned16(W) || !aligned16(X_prof) || (n > 0 && (!aligned16(out_idx) || !aligned16(workspace))))
+    return QW_ERR_ALIGNMENT;
   qw_status st = current_device(nullptr);
   if (st != QW_OK) return st;
   if (n == 0) return QW_OK;
   hipStream_t s = as_stream(stream);
-  void *scratch = nullptr;
-  const size_t bytes = (size_t)K * (2 * sizeof(double) + sizeof(int32_t));
-  QW_HIP_TRY(hipMallocAsync(&scratch, bytes, s));
-  double *sc = reinterpret_cast<double *>(scratch);
+  // workspace: scores [K] double, profile means [K] double, flags [K] int32
+  double *sc = reinterpret_cast<double *>(workspace);
   double *prof = sc + K;
   int32_t *flag = reinterpret_cast<int32_t *>(prof + K);
   const unsigned cgrid = grid_for(K, 64);
@@ -473,15 +474,13 @@ qw_status qw_select_outliers(const float *W, int N, int K, const float *X_prof, 
   if (e == hipSuccess)
     e = launch(score_finish_kernel, grid_for(K, 256), 256, 0, s, sc, K, N, (int)score,
                (const double *)prof, (double)P);
-  qw_status rs = e == hipSuccess ? rank_and_compact(sc, flag, K, n, out_idx, s) : QW_ERR_HIP;
-  hipError_t fe = hipFreeAsync(scratch, s);
-  if (rs != QW_OK || fe != hipSuccess) return QW_ERR_HIP;
-  return QW_OK;
+  return e == hipSuccess ? rank_and_compact(sc, flag, K, n, out_idx, s) : QW_ERR_HIP;
 }
 
 qw_status qw_select_outliers_ex(const void *W, qw_dtype w_dtype, int N, int K,
                                 const double *prof_abs_sum, long long prof_rows, double frac,
-                                qw_score score, int32_t *out_idx, void *stream) {
+                                qw_score score, int32_t *out_idx, void *workspace,
+                                size_t workspace_bytes, void *stream) {
   using namespace qw;
   CallScope scope;
   if (!W || !prof_abs_sum || N <= 0 || K <= 0 || prof_rows <= 0) return QW_ERR_INVALID_ARG;
@@ -491,15 +490,15 @@ qw_status qw_select_outliers_ex(const void *W, qw_dtype w_dtype, int N, int K,
   const int n = qw_outlier_count(K, frac);
   if (n < 0) return QW_ERR_INVALID_ARG;
   if (n > 0 && !out_idx) return QW_ERR_INVALID_ARG;
-  if (!aligned16(W) || !aligned16(prof_abs_sum) || (n > 0 && !aligned16(out_idx))) return QW_ERR_ALIGNMENT;
+  if (n > 0 && (!workspace || workspace_bytes < qw_select_workspace_bytes(K))) return QW_ERR_INVALID_ARG;
+  if (!aligned16(W) || !aligned16(prof_abs_sum) || (n > 0 && (!aligned16(out_idx) || !aligned16(workspace))))
+    return QW_ERR_ALIGNMENT;
   qw_status st = current_device(nullptr);
   if (st != QW_OK) return st;
   if (n == 0) return QW_OK;
   hipStream_t s = as_stream(stream);
-  void *scratch = nullptr;
-  const size_t bytes = (size_t)K * (sizeof(double) + sizeof(int32_t));
-  QW_HIP_TRY(hipMallocAsync(&scratch, bytes, s));
-  double *sc = reinterpret_cast<double *>(scratch);
+  // workspace: scores [K] double, flags [K] int32
+  double *sc = reinterpret_cast<double *>(workspace);
   int32_t *flag = reinterpret_cast<int32_t *>(sc + K);
   const unsigned cgrid = grid_for(K, 64);
   const bool l2 = score == QW_SCORE_L2;
@@ -526,10 +525,7 @@ qw_status qw_select_outliers_ex(const void *W, qw_dtype w_dtype, int N, int K,
   if (e == hipSuccess)
     e = launch(score_finish_kernel, grid_for(K, 256), 256, 0, s, sc, K, N, (int)score, prof_abs_sum,
                (double)prof_rows);
-  qw_status rs = e == hipSuccess ? rank_and_compact(sc, flag, K, n, out_idx, s) : QW_ERR_HIP;
-  hipError_t fe = hipFreeAsync(scratch, s);
-  if (rs != QW_OK || fe != hipSuccess) return QW_ERR_HIP;
-  return QW_OK;
+  return e == hipSuccess ? rank_and_compact(sc, flag, K, n, out_idx, s) : QW_ERR_HIP;
 }
 
 }  // extern "C"

@@ -747,11 +747,11 @@ qw_status launch_fmt(const PrefillArgs &a, bool f32, int cus, hipStream_t s) {
   const bool fits32 = (size_t)a.M * a.K * 2 < (1ull << 31) && (size_t)a.M * a.N * esz < (1ull << 31) &&
                       (size_t)a.N * (a.K / 2) < (1ull << 31);
   if (a.n_out == 0 && fits32) {  // W straight to registers
-    // QW_PREFILL_WIDE_TILES overrides the number of 256-wide column tiles
-    // (tests use it to run the 128-wide kernel on small shapes)
+    // the test hook QW_TUNE_PREFILL_WIDE_TILES overrides the number of
+    // 256-wide column tiles (tests run the 128-wide kernel on small shapes)
     const int nt = (a.N + 255) / 256;
-    const char *ev = getenv("QW_PREFILL_WIDE_TILES");
-    const int nw = ev ? max(0, min(atoi(ev), nt)) : wide_column_tiles(a.mt_count, a.N, cus);
+    const int forced = tune(QW_TUNE_PREFILL_WIDE_TILES);
+    const int nw = forced >= 0 ? min(forced, nt) : wide_column_tiles(a.mt_count, a.N, cus);
     const int rest = a.N - 256 * nw;
     const int nn = rest > 0 ? (rest + 127) / 128 : 0;
     if (f32) {
@@ -806,8 +806,7 @@ extern "C" qw_status qgemm_prefill(const qw_weight *w, const void *X, int M, voi
   a.n_out = w->format == QW_FMT_2BIT_G32 ? w->n_out : 0;
   a.n_out_pad = w->n_out_pad;
   a.mt_count = (M + BM - 1) / BM;
-  const char *gv = getenv("QW_PREFILL_XCD_GROUP");
-  a.xcd_group = gv ? atoi(gv) : 4;
+  a.xcd_group = 4;  // row tiles an XCD walks per column sweep
   const float *L = nf4_levels_host();
   for (int i = 0; i < 16; ++i) a.nf4[i] = L[i];
   const bool f32 = y_dtype == QW_DT_F32;

@@ -8,6 +8,7 @@
 #include <utility>
 
 #include "qw.h"
+#include "qw_tuning.h"
 
 namespace qw {
 
@@ -64,6 +65,9 @@ inline bool aligned16(const void *p) {
 }
 
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Current value of a test hook of qw_tuning.h (QW_TUNE_AUTO when unset).
+int tune(qw_tune_key key);
 
 // Checks that the current device is a gfx950 and returns its CU count.
 qw_status current_device(int *cu_count);

@@ -22,14 +22,20 @@ QW_FMT_2BIT_G32, QW_FMT_NF4_B64 = 1, 2
 QW_DT_F16, QW_DT_BF16, QW_DT_F32 = 1, 2, 3
 QW_SCORE_MEANABS, QW_SCORE_L2 = 1, 2
 
-# every function declared in include/qw.h
+# every function declared in include/qw.h and include/qw_tuning.h
 EXPORTS = [
     "qw_abi_version", "qw_status_str", "qw_time_next_call", "qw_packed_sizes", "qw_outlier_count",
-    "qw_codebook_2bit", "qw_nf4_levels", "qw_select_outliers", "qw_pack",
+    "qw_codebook_2bit", "qw_nf4_levels", "qw_select_workspace_bytes", "qw_select_outliers", "qw_pack",
     "qw_pack_ex", "qw_profile_accumulate", "qw_select_outliers_ex",
     "qw_stack_plan_bytes", "qw_stack_prepare", "qw_stack_run",
-    "qgemv_2bit", "qgemv_nf4", "qgemv_2bit_grouped", "qgemm_prefill",
+    "qgemv_2bit", "qgemv_2bit_workspace_bytes", "qgemv_2bit_ws", "qgemv_nf4", "qgemv_2bit_grouped",
+    "qgemm_prefill", "qw_tune_set", "qw_tune_get",
 ]
+
+# test hooks (include/qw_tuning.h)
+QW_TUNE_GEMV2_PATH, QW_TUNE_GEMV2_SPLIT, QW_TUNE_GEMV2_DEEP_RING = 1, 2, 3
+QW_TUNE_NF4_DEEP_RING, QW_TUNE_PREFILL_WIDE_TILES = 4, 5
+QW_TUNE_AUTO = -1
 
 
 class QwError(RuntimeError):
@@ -91,18 +97,24 @@ def lib():
         "qw_outlier_count": (c_i, [c_i, c_d]),
         "qw_codebook_2bit": (c_i, [ctypes.POINTER(ctypes.c_float)]),
         "qw_nf4_levels": (c_i, [ctypes.POINTER(ctypes.c_float)]),
-        "qw_select_outliers": (c_i, [c_p, c_i, c_i, c_p, c_i, c_d, c_i, c_p, c_p]),
+        "qw_select_workspace_bytes": (c_sz, [c_i]),
+        "qw_select_outliers": (c_i, [c_p, c_i, c_i, c_p, c_i, c_d, c_i, c_p, c_p, c_sz, c_p]),
         "qw_pack": (c_i, [c_p, W, c_p]),
         "qw_pack_ex": (c_i, [c_p, c_i, c_i, W, c_p]),
         "qw_profile_accumulate": (c_i, [c_p, c_i, c_i, c_i, c_p, c_p]),
-        "qw_select_outliers_ex": (c_i, [c_p, c_i, c_i, c_i, c_p, ctypes.c_longlong, c_d, c_i, c_p, c_p]),
+        "qw_select_outliers_ex": (c_i, [c_p, c_i, c_i, c_i, c_p, ctypes.c_longlong, c_d, c_i, c_p, c_p,
+                                        c_sz, c_p]),
         "qw_stack_plan_bytes": (c_sz, [c_i]),
         "qw_stack_prepare": (c_i, [ctypes.POINTER(qw_stack_stage), c_i, c_p, ctypes.POINTER(qw_stack)]),
         "qw_stack_run": (c_i, [ctypes.POINTER(qw_stack), c_p, c_p]),
         "qgemv_2bit": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
+        "qgemv_2bit_workspace_bytes": (c_i, [W, c_i, ctypes.POINTER(c_sz)]),
+        "qgemv_2bit_ws": (c_i, [W, c_p, c_i, c_p, c_i, c_p, c_sz, c_p]),
         "qgemv_nf4": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
         "qgemv_2bit_grouped": (c_i, [W, c_i, c_p, c_i, ctypes.POINTER(c_p), c_i, c_p]),
         "qgemm_prefill": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
+        "qw_tune_set": (c_i, [c_i, c_i]),
+        "qw_tune_get": (c_i, [c_i]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -175,6 +187,43 @@ def qw_nf4_levels():
     return np.array(out[:], dtype=np.float32)
 
 
+def qw_tune_set(key, value):
+    """Set a test hook of include/qw_tuning.h (QW_TUNE_AUTO restores the
+    automatic choice)."""
+    _check(lib().qw_tune_set(int(key), int(value)), "qw_tune_set")
+
+
+def qw_tune_get(key):
+    return int(lib().qw_tune_get(int(key)))
+
+
+class tuned:
+    """Context manager: ``with tuned(QW_TUNE_GEMV2_PATH, 0): ...`` sets a hook
+    for the block and restores its previous value afterwards."""
+
+    def __init__(self, key, value):
+        self.key, self.value = key, value
+
+    def __enter__(self):
+        self.prev = qw_tune_get(self.key)
+        qw_tune_set(self.key, self.value)
+        return self
+
+    def __exit__(self, *exc):
+        qw_tune_set(self.key, self.prev)
+        return False
+
+
+def qw_select_workspace_bytes(K):
+    return int(lib().qw_select_workspace_bytes(int(K)))
+
+
+def _select_workspace(K, device):
+    import torch
+    nb = qw_select_workspace_bytes(K)
+    return torch.empty(max(nb, 16), dtype=torch.uint8, device=device), nb
+
+
 # -------------------------------------------------------------- packed weight
 
 class PackedWeight:
@@ -241,8 +290,9 @@ def qw_select_outliers(W, X_prof, frac, score=QW_SCORE_MEANABS):
     if n < 0:
         raise ValueError("frac must be in [0, 1)")
     out = torch.empty(max(n, 1), dtype=torch.int32, device=W.device)
+    ws, nb = _select_workspace(K, W.device)
     _check(lib().qw_select_outliers(_ptr(W), N, K, _ptr(X_prof), X_prof.shape[0], float(frac),
-                                    int(score), _ptr(out), _stream()), "qw_select_outliers")
+                                    int(score), _ptr(out), _ptr(ws), nb, _stream()), "qw_select_outliers")
     return out[:n]
 
 
@@ -314,8 +364,9 @@ def qw_select_outliers_ex(W, prof_abs_sum, prof_rows, frac, score=QW_SCORE_MEANA
     if n < 0:
         raise ValueError("frac must be in [0, 1)")
     out = torch.empty(max(n, 1), dtype=torch.int32, device=W.device)
+    ws, nb = _select_workspace(K, W.device)
     _check(lib().qw_select_outliers_ex(_ptr(W), dt, N, K, _ptr(prof_abs_sum), int(prof_rows),
-                                       float(frac), int(score), _ptr(out), _stream()),
+                                       float(frac), int(score), _ptr(out), _ptr(ws), nb, _stream()),
            "qw_select_outliers_ex")
     return out[:n]
 
@@ -352,6 +403,41 @@ def qgemv_2bit(pw, x, out_dtype=None, out=None):
     v = pw.view()
     _check(lib().qgemv_2bit(ctypes.byref(v), _ptr(x), B, _ptr(y), _dt(y.dtype), _stream()),
            "qgemv_2bit")
+    return y
+
+
+def qgemv_2bit_workspace_bytes(pw, B):
+    """Workspace bytes qgemv_2bit_ws needs for this weight at batch B."""
+    n = ctypes.c_size_t(0)
+    v = pw.view()
+    _check(lib().qgemv_2bit_workspace_bytes(ctypes.byref(v), int(B), ctypes.byref(n)),
+           "qgemv_2bit_workspace_bytes")
+    return int(n.value)
+
+
+def gemv_workspace(pw, B, device="cuda"):
+    """A device workspace sized for qgemv_2bit_ws(pw, x of B rows), or None
+    when that call needs none."""
+    import torch
+    nb = qgemv_2bit_workspace_bytes(pw, B)
+    return torch.empty(nb, dtype=torch.uint8, device=device) if nb else None
+
+
+def qgemv_2bit_ws(pw, x, workspace, out_dtype=None, out=None):
+    """qgemv_2bit with a caller-owned workspace (a uint8 CUDA tensor, or None)."""
+    import torch
+    _need(x, torch.float16, "x", 2)
+    out_dtype = out_dtype or torch.float16
+    B = x.shape[0]
+    y = out if out is not None else torch.empty((B, pw.N), dtype=out_dtype, device=x.device)
+    _io_shapes(pw, x, [(y, pw.N)])
+    nb = 0
+    if workspace is not None:
+        _need(workspace, torch.uint8, "workspace")
+        nb = workspace.numel()
+    v = pw.view()
+    _check(lib().qgemv_2bit_ws(ctypes.byref(v), _ptr(x), B, _ptr(y), _dt(y.dtype), _ptr(workspace), nb,
+                               _stream()), "qgemv_2bit_ws")
     return y
 
 

@@ -37,8 +37,9 @@
  *  - pointers documented "device" must point to device memory of the
  *    current HIP device; "host" pointers to host memory. The caller owns
  *    and frees all memory it passes; nothing of it is retained after the
- *    call returns. The one library-owned buffer is the K-split workspace of
- *    qgemv_2bit (one per device, kept until the process ends).
+ *    call returns. No entry point allocates device memory: scratch space
+ *    (the selectors' scores, the partial rows of a K-split GEMV) is a
+ *    caller-owned workspace argument whose size a query function gives.
  *  - ``stream`` is a hipStream_t passed as void* (NULL = default stream).
  *    Device work is only enqueued; no entry point synchronizes.
  *  - arguments are validated on the host before anything is enqueued; on
@@ -57,7 +58,7 @@
 extern "C" {
 #endif
 
-#define QW_ABI_VERSION 1
+#define QW_ABI_VERSION 2
 
 typedef enum {
   QW_OK = 0,
@@ -118,10 +119,14 @@ const char *qw_status_str(qw_status s);
 qw_status qw_time_next_call(void *start_event, void *stop_event);
 
 /* Bytes the caller must allocate for each buffer of a packed matrix of the
- * given format and shape, and the anchor row stride, into host struct *out.
- * Host only. Errors: QW_ERR_INVALID_ARG if out is NULL, N, K <= 0, K not a
- * multiple of the group/block size (32 for 2-bit, 64 for NF4), n_out < 0,
- * n_out >= K, or n_out > 0 for NF4. */
+ * given format and shape, and the anchor row stride, into host struct *out:
+ * four 2-bit codes per byte ("Key v4.0 Innovations" of the OTF-LLM page),
+ * one fp16 (S, Z) pair per group of 32 (its section 3), n_out fp16 anchor
+ * weights per row (its section 4); NF4 two codes per byte and one fp32
+ * absmax per block of 64 ("AirQuant" README, item 2). Host only.
+ * Errors: QW_ERR_INVALID_ARG if out is NULL, N, K <= 0, K not a multiple of
+ * the group/block size (32 for 2-bit, 64 for NF4), n_out < 0, n_out >= K,
+ * or n_out > 0 for NF4. */
 qw_status qw_packed_sizes(qw_format fmt, int N, int K, int n_out, qw_sizes *out);
 
 /* Number of anchor channels for a fraction of K: floor(frac * K) in double
@@ -140,19 +145,27 @@ qw_status qw_codebook_2bit(float *out);
  * delta = 1 - (1/32 + 1/30)/2. */
 qw_status qw_nf4_levels(float *out);
 
+/* Bytes of the device workspace the two selectors need for K channels
+ * (K * 20; 0 when K <= 0). Host only. */
+size_t qw_select_workspace_bytes(int K);
+
 /* Profile-guided outlier selection (section 4 of the OTF-LLM page).
  *   W      device fp32 [N][K]  weights
  *   X_prof device fp32 [P][K]  calibration activations (P >= 1)
  *   frac   fraction of channels to keep, n = floor(frac*K) (0 <= frac < 1)
  *   out_idx device int32 [n]   receives the n highest-scoring channels in
  *          ascending order; ties in score go to the lower channel.
- * Scores are fp64 with sequential sums over rows. Uses a device scratch
- * buffer of K*20 bytes that it allocates and frees with the stream-ordered
- * allocator on ``stream``. Errors: INVALID_ARG for bad sizes or NULL
- * pointers, HIP if the allocation or a launch fails. */
+ *   workspace device scratch of workspace_bytes >= qw_select_workspace_bytes(K)
+ *          (16-byte aligned), owned by the caller; its contents on entry do
+ *          not matter and are overwritten. Calls that overlap in time must
+ *          not share it.
+ * Scores are fp64 with sequential sums over rows. Errors: INVALID_ARG for
+ * bad sizes, NULL pointers or a workspace that is too small, ALIGNMENT,
+ * UNSUPPORTED (W or X_prof of 2 GiB or more), HIP if a launch fails. */
 qw_status qw_select_outliers(const float *W, int N, int K, const float *X_prof,
                              int P, double frac, qw_score score,
-                             int32_t *out_idx, void *stream);
+                             int32_t *out_idx, void *workspace,
+                             size_t workspace_bytes, void *stream);
 
 /* Quantize and pack fp32 weights into ``dst`` (buffers allocated by the
  * caller with the sizes from qw_packed_sizes; dst->format, N, K, n_out,
@@ -220,45 +233,68 @@ qw_status qw_profile_accumulate(const void *X, qw_dtype x_dtype, int M, int K,
  * rows: the mean magnitude of channel c is prof_abs_sum[c] / prof_rows, and
  * W may be fp32, fp16 or bf16 (widened exactly). With sums from
  * qw_profile_accumulate over the same rows, in the same order, the chosen
- * channels are identical to qw_select_outliers on those rows.
+ * channels are identical to qw_select_outliers on those rows (section 4 of
+ * the OTF-LLM page).
  *   prof_abs_sum device double [K]; prof_rows >= 1 rows summed.
- * Uses K*12 bytes of stream-ordered scratch (allocated and freed on
- * ``stream``). Errors as qw_select_outliers. */
+ *   workspace    as for qw_select_outliers (qw_select_workspace_bytes(K)).
+ * Errors as qw_select_outliers. */
 qw_status qw_select_outliers_ex(const void *W, qw_dtype w_dtype, int N, int K,
                                 const double *prof_abs_sum, long long prof_rows,
                                 double frac, qw_score score, int32_t *out_idx,
+                                void *workspace, size_t workspace_bytes,
                                 void *stream);
 
-/* Decode GEMV for the 2-bit format:
+/* Decode GEMV for the 2-bit format ("Key v4.0 Innovations" of the OTF-LLM
+ * page: the packed codes are dequantized in registers inside the product;
+ * section 1: decoding streams every weight once per token; sections 2-4:
+ * codebook, per-group S and Z, fp16 anchors):
  *   y[b][n] = sum_k x_R[b][k] w_hat[n][k] + sum_o x[b][out_idx[o]] out_w[n][o]
  * for b < B, where x_R is x with the anchor channels set to zero.
  *   x  device fp16 [B][K], 1 <= B <= 8
  *   y  device [B][N], fp16 (QW_DT_F16, rounded nearest-even) or fp32
  * Accumulation is fp32. Codes are decoded in registers; nothing is
- * materialized. y must not alias x.
- * Batches whose x does not fit one workgroup whole (e.g. B >= 2 at
- * K = 27648) run with K cut into equal parts whose fp32 partial rows are
- * added in order; the partials live in a library-owned workspace, one per
- * device, kept until the process ends and grown with hipMalloc when a larger
- * call comes (B * N * parts * 4 bytes, parts <= 8). Such calls that overlap
- * on different streams of one device race on it: order them. Growth while
- * the stream is being captured into a graph is refused with INVALID_ARG:
- * run the same shape once eagerly before capturing.
- * Errors: INVALID_ARG (format mismatch, B, dtype, workspace growth during
- * capture), ALIGNMENT, UNSUPPORTED, HIP. */
+ * materialized. y must not alias x. Needs no workspace: batches whose x
+ * does not fit one workgroup whole (e.g. B >= 2 at K = 27648) run one row
+ * group at a time on the vector-ALU kernel; qgemv_2bit_ws runs them with
+ * the weights streamed once.
+ * Errors: INVALID_ARG (format mismatch, B, dtype), ALIGNMENT, UNSUPPORTED,
+ * HIP. */
 qw_status qgemv_2bit(const qw_weight *w, const void *x, int B, void *y,
                      qw_dtype y_dtype, void *stream);
 
-/* Decode GEMV for NF4: y[b][n] = sum_k x[b][k] w_hat[n][k]. Same argument
- * conventions as qgemv_2bit. */
+/* Device workspace bytes qgemv_2bit_ws needs for weight w at batch B (into
+ * host *bytes): 0 when the call runs without one, else parts * B * N * 4
+ * for the fp32 partial rows of its K parts (parts <= 8). Host only; the
+ * answer depends on the shape and on the current device. Errors as
+ * qgemv_2bit's argument checks. */
+qw_status qgemv_2bit_workspace_bytes(const qw_weight *w, int B, size_t *bytes);
+
+/* qgemv_2bit with a caller-owned device workspace (16-byte aligned,
+ * workspace_bytes long; may be NULL when workspace_bytes is 0). When the
+ * batch's x does not fit one workgroup whole and the workspace holds
+ * qgemv_2bit_workspace_bytes(w, B), K is cut into equal parts of whole
+ * 512-channel runs whose fp32 partial rows are written to the workspace and
+ * then added in part order (deterministic) into y; the weights stream once.
+ * With a smaller workspace the call runs as qgemv_2bit does. The
+ * workspace's contents on entry do not matter; calls that overlap in time
+ * (other streams, graph replays) must not share it. Same results rules and
+ * errors as qgemv_2bit. */
+qw_status qgemv_2bit_ws(const qw_weight *w, const void *x, int B, void *y,
+                        qw_dtype y_dtype, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* Decode GEMV for NF4 ("AirQuant" README, item 2: NF4 block-wise weights;
+ * dequantized in registers, as the 2-bit GEMV):
+ *   y[b][n] = sum_k x[b][k] w_hat[n][k].
+ * Same argument conventions as qgemv_2bit; needs no workspace. */
 qw_status qgemv_nf4(const qw_weight *w, const void *x, int B, void *y,
                     qw_dtype y_dtype, void *stream);
 
 /* Several 2-bit decode GEMVs that share one input x (for example the q, k
  * and v projections of one attention block), in one launch:
- *   y_i = qgemv_2bit(w_i, x) for i < count (count <= 4).
+ *   y_i = qgemv_2bit(w_i, x) for i < count (count <= 4), bit for bit.
  * All w_i must have the same K; y_i have their own N_i. Same conventions as
- * qgemv_2bit; ws and ys are host arrays of count entries. */
+ * qgemv_2bit (no workspace); ws and ys are host arrays of count entries. */
 qw_status qgemv_2bit_grouped(const qw_weight *ws, int count, const void *x,
                              int B, void *const *ys, qw_dtype y_dtype,
                              void *stream);
@@ -321,13 +357,17 @@ qw_status qw_stack_run(const qw_stack *st, uint32_t *sync, void *stream);
 /* Prefill GEMM: Y[m][n] = sum_k X[m][k] w_bf16[n][k] with
  * w_bf16 = bf16(fp32(S*C[q]+Z)) (one fused multiply-add, then nearest-even)
  * for 2-bit, bf16(fp32(absmax*L[q])) for NF4; 2-bit anchor columns use
- * bf16(out_w). Tiles of the dequantized weight are staged through LDS into
- * bf16 matrix-core instructions with fp32 accumulation.
+ * bf16(out_w). The pages are silent on prefill; the dequantization is each
+ * format's w_hat (OTF-LLM sections 2-3, AirQuant item 2) rounded to bf16.
+ * Without anchors the weights are dequantized in registers by the lanes
+ * that feed them to the bf16 matrix-core instructions (X is staged through
+ * LDS); with anchors, dequantized tiles of W and X are staged through LDS.
+ * Accumulation is fp32.
  *   X  device bf16 [M][K], M >= 1
  *   Y  device [M][N], bf16 (QW_DT_BF16, nearest-even of the fp32 result) or
  *      fp32 (QW_DT_F32)
- * Requires K to be a multiple of 64. Errors: INVALID_ARG, ALIGNMENT,
- * UNSUPPORTED, HIP. */
+ * Requires K to be a multiple of 64; needs no workspace. Errors:
+ * INVALID_ARG, ALIGNMENT, UNSUPPORTED, HIP. */
 qw_status qgemm_prefill(const qw_weight *w, const void *X, int M, void *Y,
                         qw_dtype y_dtype, void *stream);
 

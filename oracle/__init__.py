@@ -26,6 +26,12 @@ except the two marked "parity unpinned" below:
 * the GEMV/GEMM products have no worked example on the pages; they are pinned
   only through special cases (one-hot inputs, closed-form row sums, brute
   force on tiny shapes).
+* ``nf4.NF4_DELTA`` (the outermost quantile probability of the NF4 levels):
+  parity unpinned. The pages name NF4 and QLoRA but print no level, so the
+  absolute values of the table rest on this reading of the construction;
+  the tests pin only that the levels are the normal quantiles at evenly
+  spaced probabilities from delta to 1/2 (the shape of the construction),
+  not delta itself.
 """
 
 from .codebook import CODEBOOK_F32, CODEBOOK, lloyd_max_gaussian, gaussian_msqe

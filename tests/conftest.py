@@ -24,3 +24,19 @@ def gpu_available():
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture
+def tune():
+    """Setter for the library's test hooks (include/qw_tuning.h); every hook
+    set through it returns to the automatic choice after the test."""
+    from bit_weight_quantized_qw_amd import qw
+    keys = []
+
+    def set_(key, value):
+        qw.qw_tune_set(key, value)
+        keys.append(key)
+
+    yield set_
+    for k in keys:
+        qw.qw_tune_set(k, qw.QW_TUNE_AUTO)

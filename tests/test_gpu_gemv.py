@@ -56,7 +56,7 @@ def test_gemv_2bit_14b_shape_with_anchors(B):
 
 
 @pytest.mark.parametrize("B", [5, 8])
-def test_gemv_2bit_wide_batch_rows_equal_single_rows(B, monkeypatch):
+def test_gemv_2bit_wide_batch_rows_equal_single_rows(B, tune):
     """A batch that fits one matrix-core pass only without the raw x copy in
     LDS (anchors then gathered from global x) gives every row the bits of
     that row computed alone."""
@@ -65,7 +65,7 @@ def test_gemv_2bit_wide_batch_rows_equal_single_rows(B, monkeypatch):
     idx = oracle.select_outliers(W, X, 0.035)
     x = inputs.act_f16(B, 5120, workload=81)
     pw = _packed_2bit(W, idx)
-    monkeypatch.setenv("QW_GEMV_VALU", "0")
+    tune(qw.QW_TUNE_GEMV2_PATH, 0)
     yB = _run_2bit(pw, x, f32=True)
     for b in range(B):
         np.testing.assert_array_equal(yB[b], _run_2bit(pw, x[b:b + 1], f32=True)[0], err_msg=f"row {b}")
@@ -234,7 +234,7 @@ def test_timed_call_records_kernel_duration_and_same_result():
 @pytest.mark.parametrize("N,K,n_anchor,B", [(2048, 2048, 0, 1), (13824, 5120, 179, 1), (1000, 5120, 179, 3),
                                             (64, 3072, 40, 2), (300, 27648, 967, 1), (777, 4096, 0, 8),
                                             (16, 512, 5, 6), (17, 1024, 3, 7)])
-def test_gemv_2bit_matrix_core_and_vector_paths(N, K, n_anchor, B, monkeypatch):
+def test_gemv_2bit_matrix_core_and_vector_paths(N, K, n_anchor, B, tune):
     """Both kernels of qgemv_2bit (matrix-core path for K % 512 == 0 when
     the shape fits it, vector-ALU path otherwise or when forced) against the
     oracle on the same inputs."""
@@ -244,9 +244,9 @@ def test_gemv_2bit_matrix_core_and_vector_paths(N, K, n_anchor, B, monkeypatch):
     x = inputs.act_f16(B, K, workload=78)
     pw = _packed_2bit(W, idx)
     ref = _ref_2bit(W, x, idx)
-    monkeypatch.setenv("QW_GEMV_VALU", "0")
+    tune(qw.QW_TUNE_GEMV2_PATH, 0)
     y_mc = _run_2bit(pw, x, f32=True)
-    monkeypatch.setenv("QW_GEMV_VALU", "1")
+    tune(qw.QW_TUNE_GEMV2_PATH, 1)
     y_va = _run_2bit(pw, x, f32=True)
     e_mc, e_va = norm_err(y_mc, ref), norm_err(y_va, ref)
     print(f"{N}x{K} anchors={n_anchor} B={B}: matrix-core err {e_mc:.3e}, vector err {e_va:.3e}")
@@ -255,7 +255,7 @@ def test_gemv_2bit_matrix_core_and_vector_paths(N, K, n_anchor, B, monkeypatch):
 
 @pytest.mark.parametrize("N,K,n_anchor,B", [(1024, 5120, 179, 1), (2048, 2048, 0, 1), (11008, 4096, 0, 1),
                                             (1000, 5120, 179, 3), (64, 3072, 40, 2)])
-def test_gemv_2bit_ring_depth_same_bits(N, K, n_anchor, B, monkeypatch):
+def test_gemv_2bit_ring_depth_same_bits(N, K, n_anchor, B, tune):
     """The matrix-core kernel's two ring depths (prefetch slots per wave)
     change only when loads are issued, never the arithmetic: same bits."""
     W = inputs.weight(N, K, workload=79)
@@ -263,10 +263,10 @@ def test_gemv_2bit_ring_depth_same_bits(N, K, n_anchor, B, monkeypatch):
     idx = np.sort(rng.choice(K, n_anchor, replace=False)).astype(np.int32) if n_anchor else None
     x = inputs.act_f16(B, K, workload=79)
     pw = _packed_2bit(W, idx)
-    monkeypatch.setenv("QW_GEMV_VALU", "0")
-    monkeypatch.setenv("QW_GEMV_MC_DEEP", "0")
+    tune(qw.QW_TUNE_GEMV2_PATH, 0)
+    tune(qw.QW_TUNE_GEMV2_DEEP_RING, 0)
     y3 = _run_2bit(pw, x, f32=True)
-    monkeypatch.setenv("QW_GEMV_MC_DEEP", "1")
+    tune(qw.QW_TUNE_GEMV2_DEEP_RING, 1)
     y6 = _run_2bit(pw, x, f32=True)
     ref = _ref_2bit(W, x, idx)
     print(f"{N}x{K} anchors={n_anchor} B={B}: shallow err {norm_err(y3, ref):.3e} deep err {norm_err(y6, ref):.3e} "
@@ -275,15 +275,15 @@ def test_gemv_2bit_ring_depth_same_bits(N, K, n_anchor, B, monkeypatch):
 
 
 @pytest.mark.parametrize("N,K,B", [(11008, 4096, 1), (4096, 11008, 1), (300, 27648, 2), (1000, 4096, 4), (77, 640, 1)])
-def test_gemv_nf4_ring_depth_same_bits(N, K, B, monkeypatch):
+def test_gemv_nf4_ring_depth_same_bits(N, K, B, tune):
     """NF4 GEMV with 3 and 6 row slots per wave: same bits, and within the
     tolerance of the oracle."""
     W = inputs.weight(N, K, workload=82)
     x = inputs.act_f16(B, K, workload=82)
     q, a = oracle.quantize_nf4(W)
-    monkeypatch.setenv("QW_GEMV_NF4_DEEP", "0")
+    tune(qw.QW_TUNE_NF4_DEEP_RING, 0)
     y3 = _run_nf4(W, x, f32=True)
-    monkeypatch.setenv("QW_GEMV_NF4_DEEP", "1")
+    tune(qw.QW_TUNE_NF4_DEEP_RING, 1)
     y6 = _run_nf4(W, x, f32=True)
     e = norm_err(y3, oracle.gemv_nf4_ref(x, q, a))
     print(f"NF4 {N}x{K} B={B}: err {e:.3e} max |diff| {np.abs(y3 - y6).max():.3e}")

@@ -1,11 +1,15 @@
-"""GPU parity of the K-split matrix-core 2-bit GEMV. A matrix's channels are
-cut into equal parts of whole 512-channel super-chunks and its anchor chunks
-into runs, one part per matrix of a grouped launch (two launches beyond four
-parts); the parts' fp32 partial rows are added in order. Part counts forced
-through QW_GEMV_SPLIT on small ragged shapes (parts with and without
-anchors, batches 1-8), a one-hot check that every part reads its own
-channels, and the automatic choice at 5120x27648 with 967 anchors (where
-batches of 2-8 only fit as parts), all against the fp64 oracle."""
+"""GPU parity of the K-split matrix-core 2-bit GEMV (qgemv_2bit_ws with a
+caller-owned workspace). A matrix's channels are cut into equal parts of
+whole 512-channel super-chunks and its anchor chunks into runs, one part per
+matrix of a grouped launch (two launches beyond four parts); the parts' fp32
+partial rows are written to the workspace and added in order. Part counts
+forced through the QW_TUNE_GEMV2_SPLIT hook on small ragged shapes (parts
+with and without anchors, batches 1-8), a one-hot check that every part
+reads its own channels, and the automatic choice at 5120x27648 with 967
+anchors (where batches of 2-8 only fit as parts), all against the fp64
+oracle; the anchor channels chosen on the device equal the oracle's own
+selection there and at 8192x28672 (1003 anchors). Without a workspace the
+same calls run one row group at a time and stay within the bound."""
 
 import numpy as np
 import pytest
@@ -22,9 +26,13 @@ def _packed(W, idx):
     return qw.qw_pack(to_dev(W), qw.QW_FMT_2BIT_G32, idd)
 
 
-def _run(pw, x16, f32):
+def _run(pw, x16, f32, workspace=True):
+    """qgemv_2bit_ws with a workspace of the size the library asks for (or
+    none: then the call runs as qgemv_2bit)."""
     import torch
-    y = qw.qgemv_2bit(pw, f16_dev(x16), out_dtype=torch.float32 if f32 else torch.float16)
+    xd = f16_dev(x16)
+    ws = qw.gemv_workspace(pw, xd.shape[0]) if workspace else None
+    y = qw.qgemv_2bit_ws(pw, xd, ws, out_dtype=torch.float32 if f32 else torch.float16)
     torch.cuda.synchronize()
     return y.float().cpu().numpy()
 
@@ -40,9 +48,9 @@ def _anchors(K, n, seed):
     (77, 3072, 614, 3), (77, 3072, 614, 6),
     (48, 4608, 0, 3), (33, 6144, 2000, 4), (33, 6144, 2000, 6)])
 @pytest.mark.parametrize("B", [1, 3, 8])
-def test_forced_split_matches_oracle(N, K, n_anchor, ks, B, monkeypatch):
-    monkeypatch.setenv("QW_GEMV_VALU", "0")
-    monkeypatch.setenv("QW_GEMV_SPLIT", str(ks))
+def test_forced_split_matches_oracle(N, K, n_anchor, ks, B, tune):
+    tune(qw.QW_TUNE_GEMV2_PATH, 0)
+    tune(qw.QW_TUNE_GEMV2_SPLIT, ks)
     W = inputs.weight(N, K, workload=90)
     idx = _anchors(K, n_anchor, N + K)
     x = inputs.act_f16(B, K, workload=90)
@@ -58,9 +66,9 @@ def test_forced_split_matches_oracle(N, K, n_anchor, ks, B, monkeypatch):
     np.testing.assert_array_equal(y16.astype(np.float16), y32.astype(np.float16))
 
 
-def test_split_parts_read_their_own_channels(monkeypatch):
-    monkeypatch.setenv("QW_GEMV_VALU", "0")
-    monkeypatch.setenv("QW_GEMV_SPLIT", "3")
+def test_split_parts_read_their_own_channels(tune):
+    tune(qw.QW_TUNE_GEMV2_PATH, 0)
+    tune(qw.QW_TUNE_GEMV2_SPLIT, 3)
     N, K = 40, 3072
     W = inputs.weight(N, K, workload=91)
     idx = np.array([5, 700, 1500, 2047, 3000] + list(range(2100, 2400, 3)), np.int32)
@@ -82,10 +90,10 @@ def test_split_parts_read_their_own_channels(monkeypatch):
         assert norm_err(y[b], ref) <= 1e-6, k
 
 
-def test_split_fp16_inputs_at_extremes(monkeypatch):
+def test_split_fp16_inputs_at_extremes(tune):
     """Large and tiny inputs through the parts (per-group scaling of x)."""
-    monkeypatch.setenv("QW_GEMV_VALU", "0")
-    monkeypatch.setenv("QW_GEMV_SPLIT", "2")
+    tune(qw.QW_TUNE_GEMV2_PATH, 0)
+    tune(qw.QW_TUNE_GEMV2_SPLIT, 2)
     N, K = 64, 2048
     W = inputs.weight(N, K, workload=92)
     idx = _anchors(K, 70, 92)
@@ -101,55 +109,91 @@ def test_split_fp16_inputs_at_extremes(monkeypatch):
 
 @pytest.fixture(scope="module")
 def down():
+    """The 32B down projection (5120x27648, 967 anchors): the anchors are the
+    oracle's own selection (section 4 of the OTF-LLM page), and the device's
+    selection from the same profile must equal it."""
     N, K = 5120, 27648
     W = inputs.weight(N, K, workload=4, layer=0, proj=6)
     X = inputs.profile(256, K, workload=4, layer=0, proj=3)
+    want = oracle.select_outliers(W, X, 0.035)
+    assert len(want) == 967
     Wd = to_dev(W)
-    idx = qw.qw_select_outliers(Wd, to_dev(X), 0.035)
-    pw = qw.qw_pack(Wd, qw.QW_FMT_2BIT_G32, idx)
+    got = qw.qw_select_outliers(Wd, to_dev(X), 0.035).cpu().numpy()
+    np.testing.assert_array_equal(got, want, err_msg="device anchor set at 5120x27648")
+    pw = qw.qw_pack(Wd, qw.QW_FMT_2BIT_G32, to_dev(want))
     del Wd
     rows = np.sort(inputs.rng(4, 0, 6, 5).choice(N, 192, replace=False))
-    r = oracle.quantize_2bit(W[rows], idx.cpu().numpy())
+    r = oracle.quantize_2bit(W[rows], want)
     return pw, rows, r
+
+
+def test_selection_down70b_equals_oracle():
+    """8192x28672 with a 28672-channel profile: 1003 anchors, the device's
+    choice equals the oracle's."""
+    N, K = 8192, 28672
+    W = inputs.weight(N, K, workload=6)
+    X = inputs.profile(256, K, workload=6)
+    want = oracle.select_outliers(W, X, 0.035)
+    assert len(want) == 1003
+    got = qw.qw_select_outliers(to_dev(W), to_dev(X), 0.035).cpu().numpy()
+    np.testing.assert_array_equal(got, want)
 
 
 @pytest.mark.parametrize("B", [1, 2, 5, 8])
 @pytest.mark.parametrize("path", ["auto", "matrix_core"])
-def test_down_projection_batches(down, B, path, monkeypatch):
+def test_down_projection_batches(down, B, path, tune):
     """5120x27648 with 967 anchors: batches of 2-8 run as K parts (their x
-    does not fit one workgroup whole); checked on 192 sampled rows."""
+    does not fit one workgroup whole); checked on 192 sampled rows. Without
+    a workspace (qgemv_2bit) the same call runs without parts."""
     if path == "matrix_core":
-        monkeypatch.setenv("QW_GEMV_VALU", "0")
+        tune(qw.QW_TUNE_GEMV2_PATH, 0)
     pw, rows, r = down
     x = inputs.act_f16(B, 27648, workload=4, layer=0, proj=9)
-    y = _run(pw, x, True)
     ref = oracle.gemv_2bit_ref(x, r["q"], r["S"], r["Z"], r["idx"], r["W_O"])
-    e = norm_err(y[:, rows], ref)
-    print(f"down B={B} {path}: err {e:.3e}")
-    assert e <= TOL
+    for ws in (True, False):
+        y = _run(pw, x, True, workspace=ws)
+        e = norm_err(y[:, rows], ref)
+        print(f"down B={B} {path} workspace={ws}: err {e:.3e}")
+        assert e <= TOL
+
+
+def test_workspace_query_and_small_workspace():
+    """The library asks for a workspace exactly where the batch needs K parts
+    (parts * B * N * 4 bytes), and a workspace one byte short runs the call
+    as qgemv_2bit does, bit for bit."""
+    import torch
+    N, K = 64, 27648
+    W = inputs.weight(N, K, workload=96)
+    pw = _packed(W, _anchors(K, 500, 96))
+    assert qw.qgemv_2bit_workspace_bytes(pw, 1) == 0
+    for B in (2, 8):
+        nb = qw.qgemv_2bit_workspace_bytes(pw, B)
+        assert nb > 0 and nb % (B * N * 4) == 0 and nb // (B * N * 4) <= 8, (B, nb)
+        x = f16_dev(inputs.act_f16(B, K, workload=96))
+        plain = qw.qgemv_2bit(pw, x, out_dtype=torch.float32)
+        short = torch.empty(nb - 1, dtype=torch.uint8, device="cuda")
+        got = qw.qgemv_2bit_ws(pw, x, short, out_dtype=torch.float32)
+        assert torch.equal(got, plain), B
 
 
 def test_split_call_in_graph_replays_equal_eager(down):
-    """A K-split call captured in a HIP graph (after an eager call of the same
-    shape sized the workspace) replays with the eager call's bits, for new
-    inputs copied in between replays and with other work between them."""
+    """A K-split call captured in a HIP graph replays with the eager call's
+    bits, for new inputs copied in between replays and with other work
+    between them (the workspace is allocated before the capture)."""
     import torch
     pw, _, _ = down
     B = 8
+    ws = qw.gemv_workspace(pw, B)
+    assert ws is not None
     xs = [f16_dev(inputs.act_f16(B, 27648, workload=4, layer=0, proj=20 + i)) for i in range(3)]
-    eager = [qw.qgemv_2bit(pw, xi, out_dtype=torch.float32).clone() for xi in xs]
+    eager = [qw.qgemv_2bit_ws(pw, xi, ws, out_dtype=torch.float32).clone() for xi in xs]
     x = torch.empty_like(xs[0])
     y = torch.zeros((B, 5120), dtype=torch.float32, device="cuda")
     x.copy_(xs[0])
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        qw.qgemv_2bit(pw, x, out=y)
-    torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        qw.qgemv_2bit(pw, x, out=y)
+        qw.qgemv_2bit_ws(pw, x, ws, out=y)
     for rep in range(2):
         for i, xi in enumerate(xs):
             x.copy_(xi)
@@ -191,7 +235,7 @@ def test_grouped_call_of_split_matrices_equals_separate_calls():
 
 
 @pytest.mark.parametrize("forced", ["5", "9", "1"])
-def test_invalid_forced_part_count_falls_back(forced, monkeypatch):
+def test_invalid_forced_part_count_falls_back(forced, tune):
     """A forced part count that does not divide the super-chunks or does not
     fit (or 1 where the batch cannot run whole) leaves the automatic choice,
     bit for bit."""
@@ -200,7 +244,8 @@ def test_invalid_forced_part_count_falls_back(forced, monkeypatch):
     W = inputs.weight(N, K, workload=95)
     pw = _packed(W, _anchors(K, 500, 95))
     x = f16_dev(inputs.act_f16(4, K, workload=95))
-    auto = qw.qgemv_2bit(pw, x, out_dtype=torch.float32).cpu().numpy()
-    monkeypatch.setenv("QW_GEMV_SPLIT", forced)
-    got = qw.qgemv_2bit(pw, x, out_dtype=torch.float32).cpu().numpy()
+    ws = torch.empty(8 * 4 * N * 4, dtype=torch.uint8, device="cuda")  # room for 8 parts
+    auto = qw.qgemv_2bit_ws(pw, x, ws, out_dtype=torch.float32).cpu().numpy()
+    tune(qw.QW_TUNE_GEMV2_SPLIT, int(forced))
+    got = qw.qgemv_2bit_ws(pw, x, ws, out_dtype=torch.float32).cpu().numpy()
     np.testing.assert_array_equal(got, auto)

@@ -15,9 +15,9 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("valu", ["0", "1"])
-def test_graph_replays_equal_eager(valu, monkeypatch):
+def test_graph_replays_equal_eager(valu, tune):
     import torch
-    monkeypatch.setenv("QW_GEMV_VALU", valu)  # the GEMV path captured
+    tune(qw.QW_TUNE_GEMV2_PATH, int(valu))  # the GEMV path captured
     K, B, M = 1024, 2, 300
     W0 = inputs.weight(512, K, workload=90, proj=0)
     W1 = inputs.weight(256, K, workload=90, proj=1)

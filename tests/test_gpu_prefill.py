@@ -44,10 +44,10 @@ SMALL = [(300, 200, 512), (1, 1, 64), (257, 129, 128), (512, 1024, 2048), (513, 
 @pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("M,N,K", SMALL)
 @pytest.mark.parametrize("wide", [None, "0", "1"])
-def test_prefill_small(fmt, M, N, K, wide, monkeypatch):
+def test_prefill_small(fmt, M, N, K, wide, tune):
     import torch
     if wide is not None:
-        monkeypatch.setenv("QW_PREFILL_WIDE_TILES", wide)
+        tune(qw.QW_TUNE_PREFILL_WIDE_TILES, int(wide))
     W = inputs.weight(N, K, workload=80)
     X = inputs.act_bf16_bits(M, K, workload=80)
     pw = _pack(W, fmt)

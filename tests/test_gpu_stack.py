@@ -67,14 +67,14 @@ def _oracle_err(pw_w_idx, x16, y):
 
 
 @pytest.mark.parametrize("L", [1, 3])
-def test_stack_single_stages_bit_exact_grouped_within_tolerance(L, monkeypatch):
+def test_stack_single_stages_bit_exact_grouped_within_tolerance(L, tune):
     import torch
     layers, stages = _stages(L, torch.float16)
     st = qw.Stack(stages)
     st.run()
     torch.cuda.synchronize()
     assert st.error() == 0
-    monkeypatch.setenv("QW_GEMV_VALU", "0")   # the matrix-core kernel, as in the stack
+    tune(qw.QW_TUNE_GEMV2_PATH, 0)   # the matrix-core kernel, as in the stack
     for li, (w, x_attn, x_mlp, x_down, y) in enumerate(layers):
         # o reads y_q and down reads y_gate as the fused run left them
         for n, xin in (("o", y["q"]), ("down", y["gate"])):

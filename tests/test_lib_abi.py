@@ -1,5 +1,5 @@
 """CPU checks of the C ABI: libqw.so loads, exports every function that
-include/qw.h declares, its host-side constants agree with the oracle bit for
+include/qw.h and include/qw_tuning.h declare, its host-side constants agree with the oracle bit for
 bit (the two sides compute them independently), and argument validation
 returns the documented status before any device work. No kernel runs."""
 
@@ -25,9 +25,14 @@ def L():
 
 
 def _declared():
-    src = open(os.path.join(ROOT, "include", "qw.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(q\w+)\s*\(", src)) - {"qw_weight"})
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if not h.endswith(".h"):
+            continue
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(q\w+)\s*\(", src))
+    return sorted(names - {"qw_weight"})
 
 
 def test_every_declared_symbol_is_exported(L):
@@ -39,7 +44,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_abi_version_and_status_text(L):
-    assert qw.qw_abi_version() == 1
+    assert qw.qw_abi_version() == 2
     for s in range(6):
         assert qw.qw_status_str(s)
     assert qw.qw_status_str(99) == "unknown status"
@@ -110,10 +115,24 @@ def test_validation_before_device_work(L):
     # prefill needs K % 64
     v96 = _view(qw.QW_FMT_2BIT_G32, 16, 96)
     assert L.qgemm_prefill(ctypes.byref(v96), p, 4, p, qw.QW_DT_F32, s) == qw.QW_ERR_UNSUPPORTED
-    # select_outliers: bad fraction / sizes
-    assert L.qw_select_outliers(p, 4, 64, p, 2, 1.5, 1, p, s) == qw.QW_ERR_INVALID_ARG
-    assert L.qw_select_outliers(p, 4, 64, p, 0, 0.1, 1, p, s) == qw.QW_ERR_INVALID_ARG
-    assert L.qw_select_outliers(p, 4, 64, p, 2, 0.1, 7, p, s) == qw.QW_ERR_INVALID_ARG
+    # select_outliers: bad fraction / sizes / workspace
+    nb = qw.qw_select_workspace_bytes(64)
+    assert nb == 64 * 20 and qw.qw_select_workspace_bytes(0) == 0
+    assert L.qw_select_outliers(p, 4, 64, p, 2, 1.5, 1, p, p, nb, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_select_outliers(p, 4, 64, p, 0, 0.1, 1, p, p, nb, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_select_outliers(p, 4, 64, p, 2, 0.1, 7, p, p, nb, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_select_outliers(p, 4, 64, p, 2, 0.1, 1, p, p, nb - 1, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_select_outliers(p, 4, 64, p, 2, 0.1, 1, p, None, nb, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_select_outliers(p, 4, 64, p, 2, 0.1, 1, p, ctypes.c_void_p(0x1008), nb, s) \
+        == qw.QW_ERR_ALIGNMENT
+    # GEMV workspace: size query checks its arguments; a byte count without
+    # a buffer is refused
+    n = ctypes.c_size_t(7)
+    assert L.qgemv_2bit_workspace_bytes(None, 1, ctypes.byref(n)) == qw.QW_ERR_INVALID_ARG
+    assert L.qgemv_2bit_workspace_bytes(ctypes.byref(v), 9, ctypes.byref(n)) == qw.QW_ERR_INVALID_ARG
+    assert L.qgemv_2bit_workspace_bytes(ctypes.byref(v), 1, None) == qw.QW_ERR_INVALID_ARG
+    assert L.qgemv_2bit_ws(ctypes.byref(v), p, 1, p, qw.QW_DT_F16, None, 64, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qgemv_2bit_ws(ctypes.byref(v), p, 1, p, qw.QW_DT_F16, odd, 64, s) == qw.QW_ERR_ALIGNMENT
 
 
 def test_validation_of_pack_ex_and_profile_calls(L):
@@ -132,10 +151,27 @@ def test_validation_of_pack_ex_and_profile_calls(L):
     assert L.qw_profile_accumulate(p, 7, 4, 64, p, s) == qw.QW_ERR_INVALID_ARG
     assert L.qw_profile_accumulate(p, qw.QW_DT_BF16, 4, 64, None, s) == qw.QW_ERR_INVALID_ARG
     assert L.qw_profile_accumulate(p, qw.QW_DT_F32, 4, 64, ctypes.c_void_p(0x1008), s) == qw.QW_ERR_ALIGNMENT
-    # selection from sums: rows, fraction, score kind
-    assert L.qw_select_outliers_ex(p, qw.QW_DT_F16, 4, 64, p, 0, 0.1, 1, p, s) == qw.QW_ERR_INVALID_ARG
-    assert L.qw_select_outliers_ex(p, qw.QW_DT_F16, 4, 64, p, 8, 1.0, 1, p, s) == qw.QW_ERR_INVALID_ARG
-    assert L.qw_select_outliers_ex(p, qw.QW_DT_F16, 4, 64, p, 8, 0.1, 3, p, s) == qw.QW_ERR_INVALID_ARG
+    # selection from sums: rows, fraction, score kind, workspace
+    nb = qw.qw_select_workspace_bytes(64)
+    assert L.qw_select_outliers_ex(p, qw.QW_DT_F16, 4, 64, p, 0, 0.1, 1, p, p, nb, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_select_outliers_ex(p, qw.QW_DT_F16, 4, 64, p, 8, 1.0, 1, p, p, nb, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_select_outliers_ex(p, qw.QW_DT_F16, 4, 64, p, 8, 0.1, 3, p, p, nb, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_select_outliers_ex(p, qw.QW_DT_F16, 4, 64, p, 8, 0.1, 1, p, p, 8, s) == qw.QW_ERR_INVALID_ARG
+
+
+def test_tuning_hooks_are_host_only(L):
+    """The test hooks of qw_tuning.h: unknown keys and values below -1 are
+    refused; a set value reads back and QW_TUNE_AUTO restores the default."""
+    assert L.qw_tune_set(0, 1) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_tune_set(99, 1) == qw.QW_ERR_INVALID_ARG
+    assert L.qw_tune_set(qw.QW_TUNE_GEMV2_PATH, -2) == qw.QW_ERR_INVALID_ARG
+    assert qw.qw_tune_get(99) == qw.QW_TUNE_AUTO
+    for key in (qw.QW_TUNE_GEMV2_PATH, qw.QW_TUNE_GEMV2_SPLIT, qw.QW_TUNE_GEMV2_DEEP_RING,
+                qw.QW_TUNE_NF4_DEEP_RING, qw.QW_TUNE_PREFILL_WIDE_TILES):
+        assert qw.qw_tune_get(key) == qw.QW_TUNE_AUTO
+        with qw.tuned(key, 3):
+            assert qw.qw_tune_get(key) == 3
+        assert qw.qw_tune_get(key) == qw.QW_TUNE_AUTO
 
 
 def test_valid_call_without_gpu_reports_no_device(L):
