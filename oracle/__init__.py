@@ -14,6 +14,10 @@ generators. The oracle is written from the pages that define the method:
   FP16 outlier anchors (section 4).
 * "AirQuant" README, "Fundamentacao Teorica e Arquitetura" item 2 and
   "Fontes": NF4 (NormalFloat4, QLoRA) block-wise weight quantization.
+* the OTF-LLM page's "Comparative Analysis: INT4 (v3.2) vs INT2 Non-Uniform
+  (v4.0)" and "Method Comparison Table": the v3.2 INT4 format (uniform
+  symmetric grid, two codes per byte, a static channel permutation, the top
+  1% channels in FP16).
 
 Where the pages leave a step open, the reading taken is stated in the
 docstring of the function that takes it. Every function here is pinned by a
@@ -42,6 +46,9 @@ from .nf4 import (BLOCK_NF4, nf4_levels, quantize_nf4, pack_nf4, unpack_nf4,
                   dequant_nf4)
 from .outliers import (outlier_count, profile_abs_sum, profile_absmean, channel_scores,
                        select_outliers, SCORE_MEANABS, SCORE_L2)
+from .int4perm import (GROUP_INT4, QMAX_INT4, ANCHOR_FRAC_INT4, int4_permutation, permute_cols,
+                       quantize_int4, pack_int4, unpack_int4, dequant_int4, gemv_int4_ref,
+                       prefill_weight_bf16_int4)
 from .products import (gemv_2bit_ref, gemv_nf4_ref, prefill_weight_bf16_2bit,
                        prefill_weight_bf16_nf4, gemm_prefill_ref)
 
@@ -54,6 +61,9 @@ __all__ = [
     "dequant_nf4",
     "outlier_count", "profile_abs_sum", "profile_absmean", "channel_scores", "select_outliers",
     "SCORE_MEANABS", "SCORE_L2",
+    "GROUP_INT4", "QMAX_INT4", "ANCHOR_FRAC_INT4", "int4_permutation", "permute_cols",
+    "quantize_int4", "pack_int4", "unpack_int4", "dequant_int4", "gemv_int4_ref",
+    "prefill_weight_bf16_int4",
     "gemv_2bit_ref", "gemv_nf4_ref", "prefill_weight_bf16_2bit",
     "prefill_weight_bf16_nf4", "gemm_prefill_ref",
 ]
