@@ -190,6 +190,7 @@ const char *qw_status_str(qw_status s) {
     case QW_ERR_UNSUPPORTED: return "unsupported request";
     case QW_ERR_HIP: return "HIP runtime error";
     case QW_ERR_NO_DEVICE: return "no gfx950 device is current";
+    case QW_ERR_SCRATCH_LIMIT: return "request needs more than the library's static scratch array";
   }
   return "unknown status";
 }

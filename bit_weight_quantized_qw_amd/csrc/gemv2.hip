@@ -1,6 +1,14 @@
 // Host side of the 2-bit decode GEMV: validation, work split, dispatch.
 // The kernel itself (and the decode scheme) is in gemv2_kernel.h.
+#include <mutex>
+
 #include "gemv2_kernel.h"
+
+// Scratch of qgemv_2bit_static: the K-split partial rows of callers that
+// cannot allocate. Every GPU the library runs on holds its own copy until
+// the process ends. In host code this name stands for the array only as a
+// symbol: its device address (per device) comes from hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[QW_STATIC_SCRATCH_BYTES];
 
 namespace qw {
 namespace gemv2m {
@@ -233,6 +241,36 @@ qw_status qgemv_2bit_workspace_bytes(const qw_weight *w, int B, size_t *bytes) {
   // the vector-ALU path (forced by the test hook, or K % 512 != 0) needs none
   *bytes = tune(QW_TUNE_GEMV2_PATH) == 1 ? 0 : gemv2m::split_workspace_bytes(*w, B, cus);
   return QW_OK;
+}
+
+// Device address of ``scratch`` on the current device, looked up once per
+// device (with that device current) and kept.
+static qw_status static_scratch(void **out) {
+  static std::mutex mu;
+  static void *addr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return QW_ERR_NO_DEVICE;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QW_ERR_HIP;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return QW_OK;
+}
+
+qw_status qgemv_2bit_static(const qw_weight *w, const void *x, int B, void *y, qw_dtype y_dtype,
+                            void *stream) {
+  using namespace qw;
+  CallScope scope;
+  size_t need = 0;
+  QW_TRY(qgemv_2bit_workspace_bytes(w, B, &need));
+  if (need > (size_t)QW_STATIC_SCRATCH_BYTES) return QW_ERR_SCRATCH_LIMIT;
+  void *ws = nullptr;
+  if (need > 0) QW_TRY(static_scratch(&ws));
+  void *ys[1] = {y};
+  return gemv2::launch(w, 1, x, B, ys, y_dtype, ws, need, as_stream(stream));
 }
 
 qw_status qgemv_2bit_grouped(const qw_weight *ws, int count, const void *x, int B,

@@ -18,6 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqw.so")
 
 QW_OK, QW_ERR_INVALID_ARG, QW_ERR_ALIGNMENT, QW_ERR_UNSUPPORTED, QW_ERR_HIP, QW_ERR_NO_DEVICE = range(6)
+QW_ERR_SCRATCH_LIMIT = 6
+QW_STATIC_SCRATCH_BYTES = 8 << 20
 QW_FMT_2BIT_G32, QW_FMT_NF4_B64 = 1, 2
 QW_DT_F16, QW_DT_BF16, QW_DT_F32 = 1, 2, 3
 QW_SCORE_MEANABS, QW_SCORE_L2 = 1, 2
@@ -28,7 +30,8 @@ EXPORTS = [
     "qw_codebook_2bit", "qw_nf4_levels", "qw_select_workspace_bytes", "qw_select_outliers", "qw_pack",
     "qw_pack_ex", "qw_profile_accumulate", "qw_select_outliers_ex",
     "qw_stack_plan_bytes", "qw_stack_prepare", "qw_stack_run",
-    "qgemv_2bit", "qgemv_2bit_workspace_bytes", "qgemv_2bit_ws", "qgemv_nf4", "qgemv_2bit_grouped",
+    "qgemv_2bit", "qgemv_2bit_workspace_bytes", "qgemv_2bit_ws", "qgemv_2bit_static", "qgemv_nf4",
+    "qgemv_2bit_grouped",
     "qgemm_prefill", "qw_tune_set", "qw_tune_get",
 ]
 
@@ -110,6 +113,7 @@ def lib():
         "qgemv_2bit": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
         "qgemv_2bit_workspace_bytes": (c_i, [W, c_i, ctypes.POINTER(c_sz)]),
         "qgemv_2bit_ws": (c_i, [W, c_p, c_i, c_p, c_i, c_p, c_sz, c_p]),
+        "qgemv_2bit_static": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
         "qgemv_nf4": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
         "qgemv_2bit_grouped": (c_i, [W, c_i, c_p, c_i, ctypes.POINTER(c_p), c_i, c_p]),
         "qgemm_prefill": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
@@ -439,6 +443,18 @@ def qgemv_2bit_ws(pw, x, workspace, out_dtype=None, out=None):
     _check(lib().qgemv_2bit_ws(ctypes.byref(v), _ptr(x), B, _ptr(y), _dt(y.dtype), _ptr(workspace), nb,
                                _stream()), "qgemv_2bit_ws")
     return y
+
+
+def qgemv_2bit_static(pw, x, out):
+    """qgemv_2bit_ws with the library's static device scratch instead of a
+    workspace: the call allocates nothing (``out`` must be given)."""
+    import torch
+    _need(x, torch.float16, "x", 2)
+    _io_shapes(pw, x, [(out, pw.N)])
+    v = pw.view()
+    _check(lib().qgemv_2bit_static(ctypes.byref(v), _ptr(x), x.shape[0], _ptr(out), _dt(out.dtype), _stream()),
+           "qgemv_2bit_static")
+    return out
 
 
 def qgemv_nf4(pw, x, out_dtype=None, out=None):

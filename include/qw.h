@@ -66,7 +66,9 @@ typedef enum {
   QW_ERR_ALIGNMENT = 2,   /* a device pointer is not 16-byte aligned */
   QW_ERR_UNSUPPORTED = 3, /* valid request this build does not implement */
   QW_ERR_HIP = 4,         /* a HIP runtime call or launch failed */
-  QW_ERR_NO_DEVICE = 5    /* no gfx950 device is current */
+  QW_ERR_NO_DEVICE = 5,   /* no gfx950 device is current */
+  QW_ERR_SCRATCH_LIMIT = 6 /* the call needs more scratch than the library's
+                              static array holds (qgemv_2bit_static) */
 } qw_status;
 
 typedef enum { QW_FMT_2BIT_G32 = 1, QW_FMT_NF4_B64 = 2 } qw_format;
@@ -282,6 +284,25 @@ qw_status qgemv_2bit_workspace_bytes(const qw_weight *w, int B, size_t *bytes);
 qw_status qgemv_2bit_ws(const qw_weight *w, const void *x, int B, void *y,
                         qw_dtype y_dtype, void *workspace,
                         size_t workspace_bytes, void *stream);
+
+/* Bytes of the library's static device scratch array (one per device). */
+#define QW_STATIC_SCRATCH_BYTES (8u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * qgemv_2bit_ws with the library's own static device array of
+ * QW_STATIC_SCRATCH_BYTES in place of the workspace argument. It allocates
+ * nothing: no hipMalloc, no hipFree, no allocating library call. The array
+ * is one per device, held until the process ends, and keeps the last call's
+ * contents (a call overwrites every byte it reads before reading it, so
+ * nothing needs clearing). Calls that overlap in time on one device (other
+ * streams, graph replays running at once) share it and race: order them.
+ * Results are those of qgemv_2bit_ws with a large enough workspace, bit for
+ * bit. Errors: those of qgemv_2bit_ws, and QW_ERR_SCRATCH_LIMIT (nothing
+ * enqueued) when qgemv_2bit_workspace_bytes(w, B) exceeds
+ * QW_STATIC_SCRATCH_BYTES. */
+qw_status qgemv_2bit_static(const qw_weight *w, const void *x, int B, void *y,
+                            qw_dtype y_dtype, void *stream);
 
 /* Decode GEMV for NF4 ("AirQuant" README, item 2: NF4 block-wise weights;
  * dequantized in registers, as the 2-bit GEMV):
