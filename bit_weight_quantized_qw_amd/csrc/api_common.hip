@@ -111,7 +111,12 @@ qw_status check_weight_view(const qw_weight *w, int format, int K_expect) {
   if (K_expect > 0 && w->K != K_expect) return QW_ERR_INVALID_ARG;
   if (!w->codes || !w->scales) return QW_ERR_INVALID_ARG;
   if (!aligned16(w->codes) || !aligned16(w->scales)) return QW_ERR_ALIGNMENT;
-  if (w->n_out > 0) {
+  if (w->n_out > 0 && format == QW_FMT_INT4_G32) {
+    // the products read the anchors only; the permutation is qw_pack's input
+    if (!w->out_w) return QW_ERR_INVALID_ARG;
+    if (w->n_out_pad < z.n_out_pad || (w->n_out_pad & 7)) return QW_ERR_INVALID_ARG;
+    if (!aligned16(w->out_w)) return QW_ERR_ALIGNMENT;
+  } else if (w->n_out > 0) {
     if (!w->out_idx || !w->out_w || !w->out_mask) return QW_ERR_INVALID_ARG;
     if (w->n_out_pad < z.n_out_pad || (w->n_out_pad & 7)) return QW_ERR_INVALID_ARG;
     if (!aligned16(w->out_idx) || !aligned16(w->out_w) || !aligned16(w->out_mask))
@@ -212,6 +217,15 @@ qw_status qw_packed_sizes(qw_format fmt, int N, int K, int n_out, qw_sizes *out)
     if (K % 64 || n_out != 0) return QW_ERR_INVALID_ARG;
     z.codes = (size_t)N * (size_t)(K / 2);
     z.scales = (size_t)N * (size_t)(K / 64) * 4;
+  } else if (fmt == QW_FMT_INT4_G32) {
+    if (K % 32) return QW_ERR_INVALID_ARG;
+    z.codes = (size_t)N * (size_t)(K / 2);
+    z.scales = (size_t)N * (size_t)(K / 32) * 2;
+    z.out_idx = (size_t)K * 4;  // the permutation
+    if (n_out > 0) {
+      z.n_out_pad = qw::pad8(n_out);
+      z.out_w = (size_t)N * (size_t)z.n_out_pad * 2;
+    }
   } else {
     return QW_ERR_INVALID_ARG;
   }

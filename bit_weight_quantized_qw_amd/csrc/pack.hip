@@ -19,6 +19,8 @@
 // lower the group's squared error (up to the epsilon of the fit).
 #include <math.h>
 
+#include <type_traits>
+
 #include "qw_internal.h"
 
 namespace qw {
@@ -214,6 +216,46 @@ __global__ __launch_bounds__(256) void pack_nf4_kernel(
   absmax[(size_t)n * G + g] = a;
 }
 
+// INT4 (the OTF-LLM page's v3.2 format, "Comparative Analysis"): one thread
+// per group of 32 permuted positions. The weights are read in original
+// channel order through perm; positions below n_out are the fp16 anchors
+// and count as 0 here. In fp64: a = max |w|, s = fp16(a / 7) (one
+// round-to-nearest-even), q = clamp(rint(w / s), -7, 7) with the stored s
+// (rint rounds ties to even; s == 0 gives q = 0); nibble q + 8, the even
+// position in the low nibble.
+template <typename WT>
+__global__ __launch_bounds__(256) void pack_int4_kernel(
+    const WT *__restrict__ W, int N, int K, const int32_t *__restrict__ perm, int n_out,
+    uint32_t *__restrict__ codes, uint16_t *__restrict__ scales) {
+#pragma clang fp contract(off)
+  const int G = K / 32;
+  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long)N * G) return;
+  const int n = (int)(gid / G), g = (int)(gid % G);
+  const WT *row = W + (size_t)n * K;
+  double w[32];
+  double a = 0.0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int j = 32 * g + i;
+    const int c = perm[j];
+    const double v = (j < n_out || c < 0 || c >= K) ? 0.0 : (double)widen(row[c]);
+    w[i] = v;
+    a = fmax(a, fabs(v));
+  }
+  const uint16_t s16 = f64_to_f16_rne(a / 7.0);
+  const double s = (double)f16_bits_to_f32(s16);
+  uint32_t out[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    double q = 0.0;
+    if (s > 0.0) q = fmin(7.0, fmax(-7.0, __builtin_rint(w[i] / s)));
+    out[i >> 3] |= (uint32_t)((int)q + 8) << (4 * (i & 7));
+  }
+  reinterpret_cast<uint4 *>(codes)[(size_t)n * G + g] = make_uint4(out[0], out[1], out[2], out[3]);
+  scales[(size_t)n * G + g] = s16;
+}
+
 // --- outlier selection ------------------------------------------------------
 
 // Column sums over rows, in row order, in fp64: out[c] = init[c] + f(A[0][c])
@@ -324,6 +366,46 @@ __global__ __launch_bounds__(256) void rank_kernel(const double *__restrict__ sc
   if (c < K) flag[c] = (beat < n) ? 1 : 0;
 }
 
+// perm[rank(c)] = c, rank(c) = number of channels that beat c (higher
+// score, or equal score and lower index): channels by descending score.
+__global__ __launch_bounds__(256) void perm_kernel(const double *__restrict__ score, int K,
+                                                   int32_t *__restrict__ perm) {
+  __shared__ double tile[256];
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  const double s = (c < K) ? score[c] : 0.0;
+  int beat = 0;
+  for (int base = 0; base < K; base += 256) {
+    const int j = base + threadIdx.x;
+    tile[threadIdx.x] = (j < K) ? score[j] : 0.0;
+    __syncthreads();
+    const int lim = min(256, K - base);
+    for (int t = 0; t < lim; ++t) {
+      const double o = tile[t];
+      const int cj = base + t;
+      beat += (o > s || (o == s && cj < c)) ? 1 : 0;
+    }
+    __syncthreads();
+  }
+  // ranks of finite scores are distinct; NaN scores would collide, so a
+  // rank is written only in range
+  if (c < K && beat < K) perm[beat] = c;
+}
+
+// X_p[m][j] = X[m][perm[j]] for elements of ES bytes (2 or 4).
+template <int ES>
+__global__ __launch_bounds__(256) void permute_cols_kernel(const uint8_t *__restrict__ X, int M, int K,
+                                                           const int32_t *__restrict__ perm,
+                                                           uint8_t *__restrict__ Xp) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long)M * K) return;
+  const int m = (int)(i / K), j = (int)(i % K);
+  const int c = perm[j];
+  typedef typename std::conditional<ES == 2, uint16_t, uint32_t>::type T;
+  T v = 0;
+  if (c >= 0 && c < K) v = reinterpret_cast<const T *>(X)[(size_t)m * K + c];
+  reinterpret_cast<T *>(Xp)[i] = v;
+}
+
 // One workgroup: ascending compaction of flagged channels.
 __global__ __launch_bounds__(1024) void compact_kernel(const int32_t *__restrict__ flag,
                                                        int K, int n, int32_t *__restrict__ out) {
@@ -365,6 +447,17 @@ qw_status pack_typed(const WT *W, int rounds, const qw_weight *dst, hipStream_t 
       QW_HIP_TRY(launch(mask_kernel, grid_for(K / 32, 256), 256, 0, s,
                         (const int32_t *)dst->out_idx, n_out, K, dst->out_mask));
     }
+  } else if (dst->format == QW_FMT_INT4_G32) {
+    const long groups = (long)N * (K / 32);
+    QW_HIP_TRY(launch(pack_int4_kernel<WT>, grid_for(groups, 256), 256, 0, s, W, N, K,
+                      (const int32_t *)dst->out_idx, n_out, reinterpret_cast<uint32_t *>(dst->codes),
+                      reinterpret_cast<uint16_t *>(dst->scales)));
+    if (n_out > 0) {
+      // anchors: the weights of channels perm[0..n_out)
+      const long cnt = (long)N * dst->n_out_pad;
+      QW_HIP_TRY(launch(anchors_kernel<WT>, grid_for(cnt, 256), 256, 0, s, W, N, K,
+                        (const int32_t *)dst->out_idx, n_out, (int)dst->n_out_pad, dst->out_w));
+    }
   } else {
     Levels16 L;
     const float *h = nf4_levels_host();
@@ -402,6 +495,10 @@ qw_status qw_pack_ex(const void *W, qw_dtype w_dtype, int refine_rounds, const q
   if (w_dtype != QW_DT_F32 && w_dtype != QW_DT_F16 && w_dtype != QW_DT_BF16) return QW_ERR_INVALID_ARG;
   qw_status st = check_weight_view(dst, dst->format, 0);
   if (st != QW_OK) return st;
+  if (dst->format == QW_FMT_INT4_G32) {  // the permutation is an input
+    if (!dst->out_idx) return QW_ERR_INVALID_ARG;
+    if (!aligned16(dst->out_idx)) return QW_ERR_ALIGNMENT;
+  }
   if (refine_rounds < 0 || refine_rounds > QW_MAX_REFINE_ROUNDS) return QW_ERR_INVALID_ARG;
   if (dst->format != QW_FMT_2BIT_G32 && refine_rounds != 0) return QW_ERR_INVALID_ARG;
   if (!aligned16(W)) return QW_ERR_ALIGNMENT;
@@ -475,6 +572,55 @@ qw_status qw_select_outliers(const float *W, int N, int K, const float *X_prof, 
     e = launch(score_finish_kernel, grid_for(K, 256), 256, 0, s, sc, K, N, (int)score,
                (const double *)prof, (double)P);
   return e == hipSuccess ? rank_and_compact(sc, flag, K, n, out_idx, s) : QW_ERR_HIP;
+}
+
+qw_status qw_select_perm(const float *W, int N, int K, const float *X_prof, int P, qw_score score,
+                         int32_t *perm_out, void *workspace, size_t workspace_bytes, void *stream) {
+  using namespace qw;
+  CallScope scope;
+  if (!W || !X_prof || !perm_out || N <= 0 || K <= 0 || P <= 0) return QW_ERR_INVALID_ARG;
+  if ((size_t)N * K * 4 >= (1ull << 31) || (size_t)P * K * 4 >= (1ull << 31)) return QW_ERR_UNSUPPORTED;
+  if (score != QW_SCORE_MEANABS && score != QW_SCORE_L2) return QW_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < qw_select_workspace_bytes(K)) return QW_ERR_INVALID_ARG;
+  if (!aligned16(W) || !aligned16(X_prof) || !aligned16(perm_out) || !aligned16(workspace))
+    return QW_ERR_ALIGNMENT;
+  qw_status st = current_device(nullptr);
+  if (st != QW_OK) return st;
+  hipStream_t s = as_stream(stream);
+  // workspace: scores [K] double, profile sums [K] double
+  double *sc = reinterpret_cast<double *>(workspace);
+  double *prof = sc + K;
+  const unsigned cgrid = grid_for(K, 64);
+  QW_HIP_TRY(score == QW_SCORE_MEANABS
+                 ? launch(colsum_kernel<float, 0>, cgrid, 256, 0, s, W, N, K, (const double *)nullptr, sc)
+                 : launch(colsum_kernel<float, 1>, cgrid, 256, 0, s, W, N, K, (const double *)nullptr, sc));
+  QW_HIP_TRY(launch(colsum_kernel<float, 0>, cgrid, 256, 0, s, X_prof, P, K, (const double *)nullptr, prof));
+  QW_HIP_TRY(launch(score_finish_kernel, grid_for(K, 256), 256, 0, s, sc, K, N, (int)score,
+                    (const double *)prof, (double)P));
+  QW_HIP_TRY(launch(perm_kernel, grid_for(K, 256), 256, 0, s, (const double *)sc, K, perm_out));
+  return QW_OK;
+}
+
+qw_status qw_permute_cols(const void *X, qw_dtype dtype, int M, int K, const int32_t *perm, void *X_p,
+                          void *stream) {
+  using namespace qw;
+  CallScope scope;
+  if (!X || !perm || !X_p || M <= 0 || K <= 0 || X == X_p) return QW_ERR_INVALID_ARG;
+  if (dtype != QW_DT_F16 && dtype != QW_DT_BF16 && dtype != QW_DT_F32) return QW_ERR_INVALID_ARG;
+  const size_t es = dtype == QW_DT_F32 ? 4 : 2;
+  if ((size_t)M * K * es >= (1ull << 31)) return QW_ERR_UNSUPPORTED;
+  if (!aligned16(X) || !aligned16(perm) || !aligned16(X_p)) return QW_ERR_ALIGNMENT;
+  qw_status st = current_device(nullptr);
+  if (st != QW_OK) return st;
+  hipStream_t s = as_stream(stream);
+  const unsigned grid = grid_for((long)M * K, 256);
+  const uint8_t *src = reinterpret_cast<const uint8_t *>(X);
+  uint8_t *dst = reinterpret_cast<uint8_t *>(X_p);
+  if (es == 2)
+    QW_HIP_TRY(launch(permute_cols_kernel<2>, grid, 256, 0, s, src, M, K, perm, dst));
+  else
+    QW_HIP_TRY(launch(permute_cols_kernel<4>, grid, 256, 0, s, src, M, K, perm, dst));
+  return QW_OK;
 }
 
 qw_status qw_select_outliers_ex(const void *W, qw_dtype w_dtype, int N, int K,

@@ -39,8 +39,8 @@ constexpr int NT = 256;
 
 struct PrefillArgs {
   const uint16_t *X;       // [M][K] bf16
-  const uint32_t *codes;   // 2-bit: [N][K/16]; NF4: [N][K/8]
-  const void *scales;      // 2-bit: uint32 [N][K/32]; NF4: float [N][K/64]
+  const uint32_t *codes;   // 2-bit: [N][K/16]; NF4, INT4: [N][K/8]
+  const void *scales;      // 2-bit: uint32 [N][K/32]; NF4: float [N][K/64]; INT4: fp16 [N][K/32]
   const int32_t *idx;      // anchors (2-bit), may be null
   const uint16_t *wo;      // [N][n_out_pad]
   void *Y;                 // [M][N]
@@ -48,7 +48,7 @@ struct PrefillArgs {
   int mt_count;            // number of 256-row tiles along M
   int n_begin;             // first output column of this launch's tiles
   int xcd_group;           // row tiles per group of the XCD-aware tile order (0: plain order)
-  float nf4[16];
+  float nf4[16];           // level of each 4-bit code (NF4 table; u - 8 for INT4)
 };
 
 __device__ inline uint32_t f32_to_bf16_bits(float v) {
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs a) {
   const int K = a.K;
   const int KT = K / BK;
 
-  if (FMT == QW_FMT_NF4_B64) {
+  if (FMT != QW_FMT_2BIT_G32) {  // NF4 levels, or u - 8 for INT4
     for (int v = tid; v < 256; v += NT) ltab[v] = make_float2(a.nf4[v & 15], a.nf4[v >> 4]);
   }
 
@@ -200,7 +200,9 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs a) {
         }
       }
     } else {
-      const float am = __builtin_bit_cast(float, rb[8]);
+      // NF4: one fp32 absmax per 64; INT4: the fp16 scale of group h
+      const float am = FMT == QW_FMT_NF4_B64 ? __builtin_bit_cast(float, rb[8])
+                                            : f16_bits_to_f32((uint16_t)(rb[8] >> (16 * h)));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t c = rb[4 * h + i];
@@ -208,6 +210,18 @@ __global__ __launch_bounds__(NT) void prefill_kernel(PrefillArgs a) {
         for (int j = 0; j < 4; ++j) {
           const float2 l = ltab[(c >> (8 * j)) & 0xFFu];
           out[i * 4 + j] = pack_bf16x2(am * l.x, am * l.y);
+        }
+      }
+      // INT4 anchors: permuted positions below n_out take bf16(out_w)
+      const int k_lo = kt * BK + 32 * h;
+      if (FMT == QW_FMT_INT4_G32 && bvalid && k_lo < a.n_out) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int e = k_lo + 2 * q;
+          const uint16_t *wr = a.wo + (size_t)gn * a.n_out_pad;
+          const uint32_t b0 = e < a.n_out ? f32_to_bf16_bits(f16_bits_to_f32(wr[e])) : (out[q] & 0xFFFFu);
+          const uint32_t b1 = e + 1 < a.n_out ? f32_to_bf16_bits(f16_bits_to_f32(wr[e + 1])) : (out[q] >> 16);
+          out[q] = b0 | (b1 << 16);
         }
       }
     }
@@ -406,7 +420,7 @@ __global__ __launch_bounds__(256 * WM) void prefill_w_kernel(PrefillArgs a) {
   // of entry v at byte 256 v + 8 r, in bank pair r. Lane l reads replica
   // l % 16, so the table reads of 16 lanes never share a bank whatever the
   // codes (one 256-entry copy would collide about 3.5 ways per access).
-  __shared__ __attribute__((aligned(16))) char pair_tab[FMT == QW_FMT_NF4_B64 ? 256 * 256 : 16];
+  __shared__ __attribute__((aligned(16))) char pair_tab[FMT != QW_FMT_2BIT_G32 ? 256 * 256 : 16];
   const uint32_t lane_rep = 8u * (uint32_t)(threadIdx.x & 15);
 
   const int tid = threadIdx.x;
@@ -420,7 +434,7 @@ __global__ __launch_bounds__(256 * WM) void prefill_w_kernel(PrefillArgs a) {
   const int KT = K / BK;
   const int hk = lane >> 5;  // which 8 of each 16-wide k slice this lane holds
 
-  if (FMT == QW_FMT_NF4_B64) {
+  if (FMT != QW_FMT_2BIT_G32) {
     // 16-byte chunk c holds two replicas of entry c / 8
     for (int c = tid; c < 256 * 8; c += NTW) {
       const int v = c >> 3;
@@ -519,7 +533,9 @@ __global__ __launch_bounds__(256 * WM) void prefill_w_kernel(PrefillArgs a) {
       const int g = kk >> 1;
       dequant8_2bit(w[j][kk], hk, T[j][g][0], T[j][g][1], o);
     } else {
-      const float am = __builtin_bit_cast(float, w[j][8]);
+      // NF4: one fp32 absmax per 64; INT4: the fp16 scale of group kk / 2
+      const float am = FMT == QW_FMT_NF4_B64 ? __builtin_bit_cast(float, w[j][8])
+                                            : f16_bits_to_f32((uint16_t)(w[j][8] >> (16 * (kk >> 1))));
       // elements kk*16 + hk*8 .. +7 = bytes 4*(2kk+hk) .. +3 of the 32 code bytes
       const uint32_t c = hk ? w[j][2 * kk + 1] : w[j][2 * kk];
 #pragma unroll
@@ -765,7 +781,7 @@ qw_status launch_fmt(const PrefillArgs &a, bool f32, int cus, hipStream_t s) {
   }
   const int nt = (a.N + BN - 1) / BN;
   const int grid = a.mt_count * nt;
-  const size_t lds = (size_t)2 * (BM + BN) * LDA * 2 + (FMT == QW_FMT_NF4_B64 ? 256 * 8 : 0);
+  const size_t lds = (size_t)2 * (BM + BN) * LDA * 2 + (FMT != QW_FMT_2BIT_G32 ? 256 * 8 : 0);
   const void *fn = f32 ? reinterpret_cast<const void *>(&prefill_kernel<FMT, true>)
                        : reinterpret_cast<const void *>(&prefill_kernel<FMT, false>);
   QW_HIP_TRY(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
@@ -785,7 +801,8 @@ extern "C" qw_status qgemm_prefill(const qw_weight *w, const void *X, int M, voi
   CallScope scope;
   if (!w || !X || !Y || M < 1) return QW_ERR_INVALID_ARG;
   if (y_dtype != QW_DT_BF16 && y_dtype != QW_DT_F32) return QW_ERR_INVALID_ARG;
-  if (!w || (w->format != QW_FMT_2BIT_G32 && w->format != QW_FMT_NF4_B64)) return QW_ERR_INVALID_ARG;
+  if (!w || (w->format != QW_FMT_2BIT_G32 && w->format != QW_FMT_NF4_B64 && w->format != QW_FMT_INT4_G32))
+    return QW_ERR_INVALID_ARG;
   qw_status st = check_weight_view(w, w->format, 0);
   if (st != QW_OK) return st;
   if (w->K % 64) return QW_ERR_UNSUPPORTED;
@@ -803,13 +820,15 @@ extern "C" qw_status qgemm_prefill(const qw_weight *w, const void *X, int M, voi
   a.M = M;
   a.N = w->N;
   a.K = w->K;
-  a.n_out = w->format == QW_FMT_2BIT_G32 ? w->n_out : 0;
+  a.n_out = w->format == QW_FMT_NF4_B64 ? 0 : w->n_out;
   a.n_out_pad = w->n_out_pad;
   a.mt_count = (M + BM - 1) / BM;
   a.xcd_group = 4;  // row tiles an XCD walks per column sweep
+  // level of each 4-bit code: the NF4 table, or u - 8 for INT4
   const float *L = nf4_levels_host();
-  for (int i = 0; i < 16; ++i) a.nf4[i] = L[i];
+  for (int i = 0; i < 16; ++i) a.nf4[i] = w->format == QW_FMT_INT4_G32 ? (float)(i - 8) : L[i];
   const bool f32 = y_dtype == QW_DT_F32;
   if (w->format == QW_FMT_2BIT_G32) return launch_fmt<QW_FMT_2BIT_G32>(a, f32, cus, as_stream(stream));
+  if (w->format == QW_FMT_INT4_G32) return launch_fmt<QW_FMT_INT4_G32>(a, f32, cus, as_stream(stream));
   return launch_fmt<QW_FMT_NF4_B64>(a, f32, cus, as_stream(stream));
 }

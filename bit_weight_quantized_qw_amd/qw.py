@@ -20,17 +20,18 @@ LIB_PATH = os.path.join(HERE, "libqw.so")
 QW_OK, QW_ERR_INVALID_ARG, QW_ERR_ALIGNMENT, QW_ERR_UNSUPPORTED, QW_ERR_HIP, QW_ERR_NO_DEVICE = range(6)
 QW_ERR_SCRATCH_LIMIT = 6
 QW_STATIC_SCRATCH_BYTES = 8 << 20
-QW_FMT_2BIT_G32, QW_FMT_NF4_B64 = 1, 2
+QW_FMT_2BIT_G32, QW_FMT_NF4_B64, QW_FMT_INT4_G32 = 1, 2, 3
 QW_DT_F16, QW_DT_BF16, QW_DT_F32 = 1, 2, 3
 QW_SCORE_MEANABS, QW_SCORE_L2 = 1, 2
 
 # every function declared in include/qw.h and include/qw_tuning.h
 EXPORTS = [
     "qw_abi_version", "qw_status_str", "qw_time_next_call", "qw_packed_sizes", "qw_outlier_count",
-    "qw_codebook_2bit", "qw_nf4_levels", "qw_select_workspace_bytes", "qw_select_outliers", "qw_pack",
+    "qw_codebook_2bit", "qw_nf4_levels", "qw_select_workspace_bytes", "qw_select_outliers",
+    "qw_select_perm", "qw_permute_cols", "qw_pack",
     "qw_pack_ex", "qw_profile_accumulate", "qw_select_outliers_ex",
     "qw_stack_plan_bytes", "qw_stack_prepare", "qw_stack_run",
-    "qgemv_2bit", "qgemv_2bit_workspace_bytes", "qgemv_2bit_ws", "qgemv_2bit_static", "qgemv_nf4",
+    "qgemv_2bit", "qgemv_2bit_workspace_bytes", "qgemv_2bit_ws", "qgemv_2bit_static", "qgemv_nf4", "qgemv_int4",
     "qgemv_2bit_grouped",
     "qgemm_prefill", "qw_tune_set", "qw_tune_get",
 ]
@@ -102,6 +103,8 @@ def lib():
         "qw_nf4_levels": (c_i, [ctypes.POINTER(ctypes.c_float)]),
         "qw_select_workspace_bytes": (c_sz, [c_i]),
         "qw_select_outliers": (c_i, [c_p, c_i, c_i, c_p, c_i, c_d, c_i, c_p, c_p, c_sz, c_p]),
+        "qw_select_perm": (c_i, [c_p, c_i, c_i, c_p, c_i, c_i, c_p, c_p, c_sz, c_p]),
+        "qw_permute_cols": (c_i, [c_p, c_i, c_i, c_i, c_p, c_p, c_p]),
         "qw_pack": (c_i, [c_p, W, c_p]),
         "qw_pack_ex": (c_i, [c_p, c_i, c_i, W, c_p]),
         "qw_profile_accumulate": (c_i, [c_p, c_i, c_i, c_i, c_p, c_p]),
@@ -115,6 +118,7 @@ def lib():
         "qgemv_2bit_ws": (c_i, [W, c_p, c_i, c_p, c_i, c_p, c_sz, c_p]),
         "qgemv_2bit_static": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
         "qgemv_nf4": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
+        "qgemv_int4": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
         "qgemv_2bit_grouped": (c_i, [W, c_i, c_p, c_i, ctypes.POINTER(c_p), c_i, c_p]),
         "qgemm_prefill": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
         "qw_tune_set": (c_i, [c_i, c_i]),
@@ -231,7 +235,9 @@ def _select_workspace(K, device):
 # -------------------------------------------------------------- packed weight
 
 class PackedWeight:
-    """Device buffers of one packed matrix (torch tensors, caller-owned)."""
+    """Device buffers of one packed matrix (torch tensors, caller-owned).
+    out_idx holds the anchor channels (2-bit) or the channel permutation
+    (INT4); out_w the fp16 anchors; out_mask the 2-bit anchor bit mask."""
 
     def __init__(self, fmt, N, K, n_out=0, device="cuda"):
         import torch
@@ -240,9 +246,11 @@ class PackedWeight:
         self.codes = torch.empty(z["codes"], dtype=torch.uint8, device=device)
         self.scales = torch.empty(z["scales"], dtype=torch.uint8, device=device)
         self.out_idx = self.out_w = self.out_mask = None
-        if n_out:
-            self.out_idx = torch.empty(n_out, dtype=torch.int32, device=device)
+        if z["out_idx"]:
+            self.out_idx = torch.empty(z["out_idx"] // 4, dtype=torch.int32, device=device)
+        if z["out_w"]:
             self.out_w = torch.empty(z["out_w"] // 2, dtype=torch.int16, device=device)
+        if z["out_mask"]:
             self.out_mask = torch.empty(z["out_mask"] // 4, dtype=torch.int32, device=device)
 
     def view(self):
@@ -253,8 +261,9 @@ class PackedWeight:
 
     def nbytes(self):
         n = self.codes.numel() + self.scales.numel()
-        if self.n_out:
-            n += self.out_idx.numel() * 4 + self.out_w.numel() * 2 + self.out_mask.numel() * 4
+        for t in (self.out_idx, self.out_w, self.out_mask):
+            if t is not None:
+                n += t.numel() * t.element_size()
         return n
 
     # host copies in the oracle's array shapes
@@ -265,6 +274,8 @@ class PackedWeight:
         a = self.scales.cpu().numpy()
         if self.format == QW_FMT_2BIT_G32:
             return a.view(np.float16).reshape(self.N, self.K // 32, 2)
+        if self.format == QW_FMT_INT4_G32:
+            return a.view(np.float16).reshape(self.N, self.K // 32)
         return a.view(np.float32).reshape(self.N, self.K // 64)
 
     def host_out_w(self):
@@ -331,6 +342,8 @@ def qw_pack_ex(W, fmt=QW_FMT_2BIT_G32, out_idx=None, refine_rounds=0):
     of nearest-level reassignment and refit (2-bit); returns PackedWeight."""
     import torch
     dt = _need_any(W, "W", 2)
+    if fmt == QW_FMT_INT4_G32:
+        raise ValueError("the INT4 format takes a permutation: use qw_pack_int4")
     N, K = W.shape
     n_out = 0 if out_idx is None else int(out_idx.numel())
     pw = PackedWeight(fmt, N, K, n_out, device=W.device)
@@ -343,6 +356,52 @@ def qw_pack_ex(W, fmt=QW_FMT_2BIT_G32, out_idx=None, refine_rounds=0):
     v = pw.view()
     _check(lib().qw_pack_ex(_ptr(W), dt, int(refine_rounds), ctypes.byref(v), _stream()), "qw_pack_ex")
     return pw
+
+
+def qw_pack_int4(W, perm, n_out, refine_rounds=0):
+    """Quantize and pack W (N, K; fp32, fp16 or bf16, original channel order)
+    into the INT4 format with channel permutation ``perm`` (int32 (K,) CUDA
+    tensor) and the first ``n_out`` permuted channels as fp16 anchors."""
+    import torch
+    dt = _need_any(W, "W", 2)
+    _need(perm, torch.int32, "perm", 1)
+    N, K = W.shape
+    if perm.numel() != K:
+        raise ValueError("perm must have K entries")
+    pw = PackedWeight(QW_FMT_INT4_G32, N, K, int(n_out), device=W.device)
+    pw.out_idx.copy_(perm)
+    v = pw.view()
+    _check(lib().qw_pack_ex(_ptr(W), dt, int(refine_rounds), ctypes.byref(v), _stream()), "qw_pack_ex")
+    return pw
+
+
+def qw_select_perm(W, X_prof, score=QW_SCORE_MEANABS):
+    """INT4 channel permutation: channels by descending outlier score."""
+    import torch
+    _need(W, torch.float32, "W", 2)
+    _need(X_prof, torch.float32, "X_prof", 2)
+    N, K = W.shape
+    out = torch.empty(K, dtype=torch.int32, device=W.device)
+    ws, nb = _select_workspace(K, W.device)
+    _check(lib().qw_select_perm(_ptr(W), N, K, _ptr(X_prof), X_prof.shape[0], int(score), _ptr(out),
+                                _ptr(ws), nb, _stream()), "qw_select_perm")
+    return out
+
+
+def qw_permute_cols(X, perm, out=None):
+    """X_p[:, j] = X[:, perm[j]] for a (M, K) fp16/bf16/fp32 CUDA tensor."""
+    import torch
+    dt = _need_any(X, "X", 2)
+    _need(perm, torch.int32, "perm", 1)
+    M, K = X.shape
+    if perm.numel() != K:
+        raise ValueError("perm must have K entries")
+    Xp = out if out is not None else torch.empty_like(X)
+    _need(Xp, X.dtype, "out", 2)
+    if tuple(Xp.shape) != (M, K):
+        raise ValueError("out must have the shape of X")
+    _check(lib().qw_permute_cols(_ptr(X), dt, M, K, _ptr(perm), _ptr(Xp), _stream()), "qw_permute_cols")
+    return Xp
 
 
 def qw_profile_accumulate(X, abs_sum):
@@ -467,6 +526,19 @@ def qgemv_nf4(pw, x, out_dtype=None, out=None):
     v = pw.view()
     _check(lib().qgemv_nf4(ctypes.byref(v), _ptr(x), B, _ptr(y), _dt(y.dtype), _stream()),
            "qgemv_nf4")
+    return y
+
+
+def qgemv_int4(pw, x_p, out_dtype=None, out=None):
+    """INT4 GEMV; x_p (B, K) fp16 in the weight's permuted channel order."""
+    import torch
+    _need(x_p, torch.float16, "x_p", 2)
+    out_dtype = out_dtype or torch.float16
+    B = x_p.shape[0]
+    y = out if out is not None else torch.empty((B, pw.N), dtype=out_dtype, device=x_p.device)
+    _io_shapes(pw, x_p, [(y, pw.N)])
+    v = pw.view()
+    _check(lib().qgemv_int4(ctypes.byref(v), _ptr(x_p), B, _ptr(y), _dt(y.dtype), _stream()), "qgemv_int4")
     return y
 
 

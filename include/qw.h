@@ -19,6 +19,17 @@
  *    Arquitetura" item 2: NormalFloat4 (QLoRA) with a per-block absmax:
  *        w_hat[n][k] = absmax[n][k/64] * L[q[n][k]],
  *    L = 16 normalised N(0,1) quantiles in [-1, 1] (see qw_nf4_levels).
+ *  QW_FMT_INT4_G32 -- the OTF-LLM page's v3.2 INT4 format ("Comparative
+ *    Analysis: INT4 (v3.2) vs INT2 Non-Uniform (v4.0)", "Method Comparison
+ *    Table"): two 4-bit codes per byte on a uniform symmetric grid with
+ *    zero-point 0, a static permutation of the input channels, the top 1%
+ *    channels kept in fp16. Channels are stored in permuted order: position
+ *    j holds input channel perm[j] (qw_select_perm orders them by descending
+ *    outlier score), and the products take activations in that order
+ *    (x_p[b][j] = x[b][perm[j]], see qw_permute_cols):
+ *        w_hat[n][j] = s[n][j/32] * (u[n][j] - 8),  u in 1..15,
+ *    s = fp16(absmax/7) per group of 32 permuted positions; the first n_out
+ *    positions are the fp16 anchors (their codes hold the zero level).
  *
  * Memory layout in device memory (all row-major, rows = output features n):
  *  2-bit codes   uint8 [N][K/4]; byte j holds elements 4j..4j+3, element
@@ -32,6 +43,12 @@
  *                channel k is an anchor (derived from out_idx by qw_pack).
  *  NF4 codes     uint8 [N][K/2]; low nibble = element 2j, high = 2j+1.
  *  NF4 scales    float [N][K/64] (absmax per block of 64 along K).
+ *  INT4 codes    uint8 [N][K/2]; low nibble = permuted position 2j, high =
+ *                2j+1; nibble u = q + 8 with q in -7..7.
+ *  INT4 scales   fp16 [N][K/32] (one per group of 32 permuted positions).
+ *  INT4 anchors  out_w fp16 [N][n_out_pad]: the weights of permuted
+ *                positions 0..n_out-1 (padding zero); out_idx int32 [K] is
+ *                the permutation (read by qw_pack only); out_mask unused.
  *
  * Conventions for every entry point:
  *  - pointers documented "device" must point to device memory of the
@@ -71,7 +88,7 @@ typedef enum {
                               static array holds (qgemv_2bit_static) */
 } qw_status;
 
-typedef enum { QW_FMT_2BIT_G32 = 1, QW_FMT_NF4_B64 = 2 } qw_format;
+typedef enum { QW_FMT_2BIT_G32 = 1, QW_FMT_NF4_B64 = 2, QW_FMT_INT4_G32 = 3 } qw_format;
 typedef enum { QW_DT_F16 = 1, QW_DT_BF16 = 2, QW_DT_F32 = 3 } qw_dtype;
 
 /* Outlier channel score ("Profile-Guided Activation Outliers", section 4):
@@ -82,7 +99,8 @@ typedef enum { QW_SCORE_MEANABS = 1, QW_SCORE_L2 = 2 } qw_score;
 
 /* Non-owning view of one packed weight matrix. All pointers are device
  * pointers owned by the caller. For NF4, out_idx/out_w are unused and n_out
- * must be 0. */
+ * must be 0. For INT4, out_idx is the channel permutation [K] (needed by
+ * qw_pack only), out_w the anchors [N][n_out_pad], out_mask unused. */
 typedef struct {
   int32_t format;     /* qw_format */
   int32_t N, K;       /* output features, input features */
@@ -90,7 +108,7 @@ typedef struct {
   int32_t n_out_pad;  /* row stride of out_w in elements (multiple of 8) */
   uint8_t *codes;     /* see layout above */
   void *scales;       /* 2-bit: uint16 [N][K/32][2]; NF4: float [N][K/64] */
-  int32_t *out_idx;   /* [n_out] or NULL when n_out == 0 */
+  int32_t *out_idx;   /* [n_out] or NULL when n_out == 0; INT4: perm [K] */
   uint16_t *out_w;    /* fp16 [N][n_out_pad] or NULL when n_out == 0 */
   uint32_t *out_mask; /* [K/32] or NULL when n_out == 0 */
 } qw_weight;
@@ -125,10 +143,13 @@ qw_status qw_time_next_call(void *start_event, void *stop_event);
  * four 2-bit codes per byte ("Key v4.0 Innovations" of the OTF-LLM page),
  * one fp16 (S, Z) pair per group of 32 (its section 3), n_out fp16 anchor
  * weights per row (its section 4); NF4 two codes per byte and one fp32
- * absmax per block of 64 ("AirQuant" README, item 2). Host only.
+ * absmax per block of 64 ("AirQuant" README, item 2); INT4 two codes per
+ * byte, one fp16 scale per group of 32, the permutation (K int32) as
+ * out_idx and n_out fp16 anchors per row ("Comparative Analysis" of the
+ * OTF-LLM page). Host only.
  * Errors: QW_ERR_INVALID_ARG if out is NULL, N, K <= 0, K not a multiple of
- * the group/block size (32 for 2-bit, 64 for NF4), n_out < 0, n_out >= K,
- * or n_out > 0 for NF4. */
+ * the group/block size (32 for 2-bit and INT4, 64 for NF4), n_out < 0,
+ * n_out >= K, or n_out > 0 for NF4. */
 qw_status qw_packed_sizes(qw_format fmt, int N, int K, int n_out, qw_sizes *out);
 
 /* Number of anchor channels for a fraction of K: floor(frac * K) in double
@@ -169,6 +190,28 @@ qw_status qw_select_outliers(const float *W, int N, int K, const float *X_prof,
                              int32_t *out_idx, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+/* The channel permutation of the INT4 format ("Global Static Permutation"
+ * of the OTF-LLM page's v3.2 engine): perm_out[j] = the channel of rank j
+ * by descending outlier score (the section-4 score of qw_select_outliers,
+ * same arguments and arithmetic), ties to the lower channel, so its first
+ * floor(0.01 K) entries are the top-1% channels the format keeps in fp16.
+ *   W, X_prof, score, workspace: as qw_select_outliers
+ *   perm_out device int32 [K]
+ * Errors as qw_select_outliers. */
+qw_status qw_select_perm(const float *W, int N, int K, const float *X_prof, int P,
+                         qw_score score, int32_t *perm_out, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/* Columns of X in permuted order: X_p[m][j] = X[m][perm[j]] (the order in
+ * which the INT4 products take their activations).
+ *   X      device [M][K], elements of dtype (F16, BF16 or F32)
+ *   perm   device int32 [K], a permutation of 0..K-1 (not checked; entries
+ *          out of range read zero)
+ *   X_p    device [M][K] of the same dtype; must not alias X
+ * Errors: INVALID_ARG, ALIGNMENT, UNSUPPORTED (X of 2 GiB or more), HIP. */
+qw_status qw_permute_cols(const void *X, qw_dtype dtype, int M, int K, const int32_t *perm,
+                          void *X_p, void *stream);
+
 /* Quantize and pack fp32 weights into ``dst`` (buffers allocated by the
  * caller with the sizes from qw_packed_sizes; dst->format, N, K, n_out,
  * n_out_pad must describe them).
@@ -183,6 +226,13 @@ qw_status qw_select_outliers(const float *W, int N, int K, const float *X_prof,
  * (section 3); S and Z rounded once to fp16 (nearest-even, subnormals kept).
  * NF4: per block of 64, absmax a = max |w|; q = number of level midpoints
  * t_j with w > t_j * a (nearest level, ties low); a == 0 gives q = 7.
+ * INT4: dst->out_idx holds the permutation (device int32 [K], a
+ * permutation of 0..K-1); W stays in its original channel order and is
+ * read through it. Positions j < n_out are the anchors: out_w = fp16 of the
+ * weight, nearest-even; their codes are the zero level. Per group of 32
+ * permuted positions (anchors counted as 0), in fp64: a = max |w|,
+ * s = fp16(a / 7) (nearest-even), q = clamp(rint(w / s), -7, 7) with the
+ * stored s (rint: nearest, ties to even; s == 0 gives q = 0).
  * The result is bit-identical to the reference quantizer. Errors:
  * INVALID_ARG, ALIGNMENT, HIP. out_idx ordering is not checked here (the
  * Python binding checks it). */
@@ -304,6 +354,19 @@ qw_status qgemv_2bit_ws(const qw_weight *w, const void *x, int B, void *y,
 qw_status qgemv_2bit_static(const qw_weight *w, const void *x, int B, void *y,
                             qw_dtype y_dtype, void *stream);
 
+/* Decode GEMV for the INT4 format (the OTF-LLM page's v3.2 engine,
+ * "Comparative Analysis" and "Method Comparison Table"; dequantized in
+ * registers inside the product as the 2-bit GEMV):
+ *   y[b][n] = sum_j x_p[b][j] w_hat[n][j] + sum_{o < n_out} x_p[b][o] out_w[n][o]
+ * with x_p the activations in permuted channel order (qw_permute_cols).
+ *   x_p device fp16 [B][K], 1 <= B <= 8
+ *   y   device [B][N], fp16 (nearest-even) or fp32
+ * fp32 accumulation; no workspace. Batches whose x does not fit one
+ * workgroup whole run as row groups. Errors: INVALID_ARG, ALIGNMENT,
+ * UNSUPPORTED, HIP. */
+qw_status qgemv_int4(const qw_weight *w, const void *x_p, int B, void *y,
+                     qw_dtype y_dtype, void *stream);
+
 /* Decode GEMV for NF4 ("AirQuant" README, item 2: NF4 block-wise weights;
  * dequantized in registers, as the 2-bit GEMV):
  *   y[b][n] = sum_k x[b][k] w_hat[n][k].
@@ -377,8 +440,9 @@ qw_status qw_stack_run(const qw_stack *st, uint32_t *sync, void *stream);
 
 /* Prefill GEMM: Y[m][n] = sum_k X[m][k] w_bf16[n][k] with
  * w_bf16 = bf16(fp32(S*C[q]+Z)) (one fused multiply-add, then nearest-even)
- * for 2-bit, bf16(fp32(absmax*L[q])) for NF4; 2-bit anchor columns use
- * bf16(out_w). The pages are silent on prefill; the dequantization is each
+ * for 2-bit, bf16(fp32(absmax*L[q])) for NF4, bf16(s*q) for INT4 (exact in
+ * fp32, then nearest-even); 2-bit and INT4 anchor columns use bf16(out_w).
+ * For INT4, X is given in permuted channel order (qw_permute_cols). The pages are silent on prefill; the dequantization is each
  * format's w_hat (OTF-LLM sections 2-3, AirQuant item 2) rounded to bf16.
  * Without anchors the weights are dequantized in registers by the lanes
  * that feed them to the bf16 matrix-core instructions (X is staged through
