@@ -22,7 +22,11 @@ synthetic input for the chosen workload:
       with a caller-owned workspace);
   decode32b_stack_fused   -- the same token as one persistent launch with a
       device-wide barrier between its 256 stages;
-  prefill70b_nf4 / prefill70b_2bit -- 2048x8192 bf16 times 28672x8192;
+  decode14b_int4_b{1,8}   -- the v3.2 INT4 format at 13824x5120: channels
+      permuted by descending outlier score, the top 1% (51) as fp16 anchors,
+      activations given in permuted order;
+  prefill70b_nf4 / prefill70b_2bit / prefill70b_int4 -- 2048x8192 bf16 times
+      28672x8192 (INT4: X in permuted channel order);
   prep_llama7b_refine5    -- preparing the 11008x4096 weight from fp16: device
       profile sums over 256 calibration rows, 3.5% anchor selection, 2-bit
       pack with 5 refinement rounds (value: fp16 weight GB/s; the packer is
@@ -107,6 +111,11 @@ def _gemv2_bytes(N, K, n_out, B):
 
 def _nf4_bytes(N, K, B):
     return N * K // 2 + N * (K // 64) * 4 + B * K * 2 + B * N * 2
+
+
+def _int4_bytes(N, K, n_out, B):
+    pad = (n_out + 7) // 8 * 8 if n_out else 0
+    return N * K // 2 + N * (K // 32) * 2 + N * pad * 2 + B * K * 2 + B * N * 2
 
 
 def _copies(pw, n):
@@ -274,6 +283,54 @@ class Down70b(Decode14b):
     ORACLE_ROWS = 512
 
 
+class Decode14bInt4(Workload):
+    """The v3.2 INT4 format at the 14B decode shape: channel permutation from
+    a spiked calibration profile, the top 1% channels as fp16 anchors."""
+    N, K = 13824, 5120
+
+    def __init__(self, B):
+        import torch
+        from bit_weight_quantized_qw_amd import inputs, qw
+        self.qw, self.B = qw, B
+        self.name = f"decode14b_int4_b{B}"
+        self.Wh = inputs.weight(self.N, self.K, workload=3)
+        self.Xp = inputs.profile(256, self.K, workload=3)
+        Wd = torch.from_numpy(self.Wh).cuda()
+        perm = qw.qw_select_perm(Wd, torch.from_numpy(self.Xp).cuda())
+        self.n_out = qw.qw_outlier_count(self.K, 0.01)
+        p = qw.qw_pack_int4(Wd, perm, self.n_out)
+        del Wd
+        self.R = max(2, math.ceil(ROTATE_BYTES / p.nbytes()))
+        self.p = _copies(p, self.R)
+        x = torch.from_numpy(inputs.act_f16(B, self.K, workload=3).view(np.int16)).cuda().view(torch.float16)
+        self.x = qw.qw_permute_cols(x, perm)
+        self.perm_h = perm.cpu().numpy()
+        self.y = torch.empty((B, self.N), dtype=torch.float16, device="cuda")
+
+    def launches(self, i):
+        r = i % self.R
+        return [("qgemv_int4", lambda: self.qw.qgemv_int4(self.p[r], self.x, out=self.y))]
+
+    def kernel_amount(self):
+        return {"qgemv_int4": _int4_bytes(self.N, self.K, self.n_out, self.B)}
+
+    def step_amount(self):
+        return self.kernel_amount()["qgemv_int4"]
+
+    def config(self):
+        return {"workload": self.name, "N": self.N, "K": self.K, "batch": self.B, "anchors": self.n_out,
+                "formats": ["int4_g32_perm"], "rotate_copies": self.R}
+
+    def cpu_baseline(self):
+        import oracle
+        from bit_weight_quantized_qw_amd import inputs
+        r = oracle.quantize_int4(self.Wh, self.perm_h, self.n_out)
+        c = oracle.pack_int4(r["q"])
+        x_p = oracle.permute_cols(inputs.act_f16(self.B, self.K, workload=3), self.perm_h)
+        return _time_oracle(lambda: oracle.gemv_int4_ref(x_p, oracle.unpack_int4(c), r["s"], r["W_O"]),
+                            self.step_amount(), f"full {self.N}x{self.K} steps, batch {self.B}")
+
+
 class Decode32bStack(Workload):
     """64 layers x {qkv (grouped), o, gate+up (grouped), down}, batch 1.
     One token is 256 launches against distinct per-layer weights."""
@@ -424,14 +481,22 @@ class Prefill70b(Workload):
         from bit_weight_quantized_qw_amd import inputs, qw
         self.qw = qw
         self.fmt = fmt
-        self.name = "prefill70b_" + ("nf4" if fmt == qw.QW_FMT_NF4_B64 else "2bit")
+        self.name = "prefill70b_" + {qw.QW_FMT_NF4_B64: "nf4", qw.QW_FMT_2BIT_G32: "2bit",
+                                     qw.QW_FMT_INT4_G32: "int4"}[fmt]
         W = inputs.torch_weight(self.N, self.K, workload=5)
-        self.p = qw.qw_pack(W, fmt)
-        del W
         Xb = inputs.act_bf16_bits(self.M, self.K, workload=5)
         self.X = torch.from_numpy(Xb.view(np.int16)).cuda().view(torch.bfloat16)
+        if fmt == qw.QW_FMT_INT4_G32:  # a fixed seeded permutation, no anchors
+            self.perm_h = np.random.default_rng(5).permutation(self.K).astype(np.int32)
+            perm = torch.from_numpy(self.perm_h).cuda()
+            self.p = qw.qw_pack_int4(W, perm, 0)
+            self.X = qw.qw_permute_cols(self.X, perm)
+        else:
+            self.p = qw.qw_pack(W, fmt)
+        del W
         self.Y = torch.empty((self.M, self.N), dtype=torch.bfloat16, device="cuda")
-        self.Xb = Xb
+        # the oracle's input: X in the order the kernel takes it
+        self.Xb = Xb[:, self.perm_h] if fmt == qw.QW_FMT_INT4_G32 else Xb
 
     def launches(self, i):
         return [("qgemm_prefill", lambda: self.qw.qgemm_prefill(self.p, self.X, out=self.Y))]
@@ -456,6 +521,10 @@ class Prefill70b(Workload):
             q, a = oracle.quantize_nf4(W)
             c = oracle.pack_nf4(q)
             wb = lambda: oracle.prefill_weight_bf16_nf4(oracle.unpack_nf4(c), a)
+        elif self.fmt == self.qw.QW_FMT_INT4_G32:
+            r = oracle.quantize_int4(W, self.perm_h, 0)
+            c = oracle.pack_int4(r["q"])
+            wb = lambda: oracle.prefill_weight_bf16_int4(oracle.unpack_int4(c), r["s"], r["W_O"])
         else:
             r = oracle.quantize_2bit(W)
             c = oracle.pack_2bit(r["q"])
@@ -598,7 +667,9 @@ WORKLOADS = {
     "down70b_b1": lambda: Down70b(1), "down70b_b8": lambda: Down70b(8),
     "decode32b_stack": Decode32bStack,
     "decode32b_stack_fused": Decode32bStackFused,
+    "decode14b_int4_b1": lambda: Decode14bInt4(1), "decode14b_int4_b8": lambda: Decode14bInt4(8),
     "prefill70b_nf4": lambda: Prefill70b(2), "prefill70b_2bit": lambda: Prefill70b(1),
+    "prefill70b_int4": lambda: Prefill70b(3),
     "prep_llama7b_refine5": PrepLlama7b,
     "copy_calib": CopyCalib,
 }
@@ -750,7 +821,7 @@ def main():
         pf = Prefill70b(1)
         log(f"workload {pf.name}: setup done")
         torch.cuda.synchronize()
-        p = measure(pf, pf.steps, pf.warmup, args.traffic_json)
+        p = measure(pf, min(pf.steps, steps), min(pf.warmup, warmup), args.traffic_json)
         out["prefill"] = {k: p[k] for k in ("value", "unit", "steps", "warmup", "ms_per_step", "dtype",
                                            "config", "roofline", "kernels", "step_timing")}
         log(f"workload {pf.name}: {p['ms_per_step']} ms per call")
