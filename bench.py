@@ -796,6 +796,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true",
                     help="leave out the prefill object of the default workload's line")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    ap.add_argument("--tune", action="append", default=[], metavar="NAME=VALUE",
+                    help="set a library test hook for A/B runs (qw_tuning.h), e.g. "
+                         "GEMV2_PATH=1 for the vector-ALU 2-bit GEMV; repeatable")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -808,6 +811,15 @@ def main():
         sys.exit(2)
     from bit_weight_quantized_qw_amd import qw
     qw.lib()  # fail loudly if libqw.so is missing
+    tuned = {}
+    for t in args.tune:
+        name, _, val = t.partition("=")
+        key = getattr(qw, "QW_TUNE_" + name.upper(), None)
+        if key is None or not val.lstrip("-").isdigit():
+            print(f"unknown --tune {t}", file=sys.stderr)
+            sys.exit(2)
+        qw.qw_tune_set(key, int(val))
+        tuned[name.upper()] = int(val)
 
     wl = WORKLOADS[args.workload]()
     log(f"workload {wl.name}: setup done")
@@ -815,6 +827,8 @@ def main():
     warmup = args.warmup if args.warmup is not None else wl.warmup
     torch.cuda.synchronize()
     out = measure(wl, steps, warmup, args.traffic_json)
+    if tuned:
+        out["tune"] = tuned
     log(f"workload {wl.name}: {out['ms_per_step']} ms per step")
     if wl.name == "decode32b_stack" and not args.no_prefill:
         # the other half of the metric, timed in the same run

@@ -196,7 +196,7 @@ struct Cursor {
 };
 
 struct Stream {
-  int n_units, W, L, NA;
+  int n_units, W, L, NA, nw;  // nw: waves of the workgroup
   __device__ int unit_len(int split) const {
     return L + (split < NA ? (NA - 1 - split) / W + 1 : 0);
   }
@@ -211,8 +211,8 @@ struct Stream {
   }
   __device__ void advance(Cursor &c) const {
     if (++c.step >= c.len) {
-      c.unit += kWaves;
-      c.split += kWaves;
+      c.unit += nw;
+      c.split += nw;
       while (c.split >= W) {
         c.split -= W;
         ++c.tile;
@@ -221,6 +221,13 @@ struct Stream {
       c.len = unit_len(c.split);
     }
   }
+};
+
+// One ring slot: three 16-byte loads per lane (code step: codes of 32
+// groups' halves and their S/Z words; anchor step: three pieces of 8 anchor
+// weights).
+struct Slot {
+  u32x4 c0, c1, c2;
 };
 
 // Select among four values that are all read (so the reads are not
@@ -237,11 +244,19 @@ __device__ inline T sel4(int i, T v0, T v1, T v2, T v3) {
 // One workgroup's share (workgroup index bid of the launch the Args were
 // planned for) of a grouped GEMV, with the group's LDS at lds.
 // XR: raw x kept in LDS for the anchor gather (a.xraw == 1); false only for
-// batches that fit one pass without it.
-template <int B, int P, bool MULTI, bool XC = false, bool XR = true>
+// batches that fit one pass without it. NT: threads of the workgroup.
+template <int B, int P, bool MULTI, bool XC = false, bool XR = true, int NT = kThreads>
 __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr int NW = NT / 64;
+  // prologue items per thread: the same totals as at kThreads threads
+  constexpr int XI = kXItems * kThreads / NT, IX = kIdxItems * kThreads / NT;
+  // the thread index through an empty asm: values derived from it are
+  // computed per call, so a persistent kernel that runs many bodies does not
+  // keep them live (and spilled) across its whole loop
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   int mi = 0;
   if (MULTI) {
@@ -295,7 +310,7 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
   const int j = lane & 15;  // output row in the tile; A row
   const int g = lane >> 4;  // slot (group) of this lane's codes and D
   // ---- stream bookkeeping (wave-uniform) ----
-  Stream st{n_units, W, L, NA};
+  Stream st{n_units, W, L, NA, NW};
 
   // ---- per-lane load offsets ----
   const uint32_t rb_c = (uint32_t)ldk / 4;         // code bytes per row
@@ -307,15 +322,10 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
   const uint32_t n_sz = (uint32_t)((size_t)M.N * rb_s - (uint32_t)kbase / 8);
   const uint32_t n_wo = (uint32_t)((size_t)M.N * rb_a - (uint32_t)abase * 2);
 
-  // ring slot = three 16-byte loads per lane. Code step: lane (row j,
-  // slot g) takes groups 16 sc + 4g .. +3 of its row: codes bytes [32g, 32g+32)
-  // of the super-chunk's 128 and their four S/Z words. Anchor step: three
-  // pieces of 8 anchor weights. One branch-free issue path: descriptor and
-  // offsets are picked per step kind.
-  struct Slot {
-    u32x4 c0, c1, c2;
-  };
-  Slot ring[P];
+  // ring slot: code step: lane (row j, slot g) takes groups 16 sc + 4g ..
+  // +3 of its row: codes bytes [32g, 32g+32) of the super-chunk's 128 and
+  // their four S/Z words. Anchor step: three pieces of 8 anchor weights. One
+  // branch-free issue path: descriptor and offsets are picked per step kind.
   auto issue = [&](Slot &dst, const Cursor &c) __attribute__((always_inline)) {
     const bool live = c.unit < n_units;
     const int tile = t0 + (live ? c.tile : 0);
@@ -354,15 +364,15 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
   const auto r_x = rsrc(a.x, (uint32_t)((size_t)B * ldk * 2));
   const auto r_mask = rsrc(M.mask, M.mask ? (uint32_t)G * 4 : 0u);
   const auto r_idx = rsrc(M.idx, (uint32_t)M.n_out * 4);
-  u32x4 xv[kXItems];
-  uint32_t mk[kXItems];
+  u32x4 xv[XI];
+  uint32_t mk[XI];
   const bool has_mask = M.mask != nullptr;
 #pragma unroll
-  for (int q = 0; q < kXItems; ++q) {
+  for (int q = 0; q < XI; ++q) {
     xv[q] = u32x4{0, 0, 0, 0};
     mk[q] = 0;
-    if (q * kThreads < n_items) {  // uniform; these are the wave's first loads
-      const int it = q * kThreads + (int)threadIdx.x;
+    if (q * NT < n_items) {  // uniform; these are the wave's first loads
+      const int it = q * NT + tid;
       const bool ok = it < n_items;
       const int bg = it >> 2, qt = it & 3;
       int b = 0;
@@ -374,17 +384,18 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
       if (has_mask) mk[q] = ld1(r_mask, ok ? (uint32_t)gr * 4 : kOob, 0);
     }
   }
-  uint32_t aidx[kIdxItems];  // valid where q * kThreads + tid < n_out
+  uint32_t aidx[IX];  // valid where q * NT + tid < n_out
 #pragma unroll
-  for (int q = 0; q < kIdxItems; ++q) {
+  for (int q = 0; q < IX; ++q) {
     aidx[q] = 0;
-    if (q * kThreads < M.n_out) {  // uniform
-      const int o = q * kThreads + (int)threadIdx.x;
+    if (q * NT < M.n_out) {  // uniform
+      const int o = q * NT + tid;
       aidx[q] = ld1(r_idx, o < M.n_out ? (uint32_t)o * 4 : kOob, 0);
     }
   }
   // ---- weight prefetch: the first P steps (every ring load is
   //      unconditional, so the waits below count exactly) ----
+  Slot ring[P];
   Cursor cl = st.start(wave);
   __builtin_amdgcn_sched_barrier(0);
   constexpr int E = kEarly < P ? kEarly : P;
@@ -400,9 +411,9 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
     const float C0 = -1.52f, C1 = -0.45f, C2 = 0.45f;
     const float d1 = C1 - C0, d3 = (C2 - C0) - 2.0f * d1;
 #pragma unroll
-    for (int q = 0; q < kXItems; ++q) {
-      if (q * kThreads < n_items) {  // uniform: whole quads stay together
-        const int it = q * kThreads + (int)threadIdx.x;
+    for (int q = 0; q < XI; ++q) {
+      if (q * NT < n_items) {  // uniform: whole quads stay together
+        const int it = q * NT + tid;
         const bool ok = it < n_items;
         const int bg = it >> 2, qt = it & 3;
         int b = 0;
@@ -458,12 +469,12 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
         }
       }
     }
-    if (threadIdx.x < 8) reinterpret_cast<uint32_t *>(zero)[threadIdx.x] = 0u;
-    if (XR && threadIdx.x < 8 * B) xraw[(threadIdx.x >> 3) * KX + K + (threadIdx.x & 7)] = 0;
+    if (tid < 8) reinterpret_cast<uint32_t *>(zero)[tid] = 0u;
+    if (XR && tid < 8 * B) xraw[(tid >> 3) * KX + K + (tid & 7)] = 0;
 #pragma unroll
-    for (int q = 0; q < kIdxItems; ++q) {
-      const int o = q * kThreads + (int)threadIdx.x;
-      if (q * kThreads < a.xo_len && o < a.xo_len) aidx_l[o] = (int)aidx[q];
+    for (int q = 0; q < IX; ++q) {
+      const int o = q * NT + tid;
+      if (q * NT < a.xo_len && o < a.xo_len) aidx_l[o] = (int)aidx[q];
     }
   }
   // LDS-only barrier: the weight prefetch stays in flight
@@ -479,7 +490,7 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
   // anchor x gathered once (zero past n_out; indices clamped to the zeros
   // at K), then a second LDS-only barrier (none without anchors)
   if (a.xo_len > 0) {  // uniform
-    for (int o = threadIdx.x; o < a.xo_len; o += kThreads) {
+    for (int o = tid; o < a.xo_len; o += NT) {
       // XR only for unsplit launches (ldk == K)
       const uint32_t ci = o < M.n_out ? min((uint32_t)aidx_l[o], (uint32_t)ldk) : (uint32_t)ldk;
       if (XR) {
@@ -600,7 +611,7 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
   // the end reads through a zero-size descriptor); the last round only
   // drains the ring, so at most P - 1 refills per wave are dead.
   int n_steps = 0;
-  for (int u = wave; u < n_units; u += kWaves) n_steps += st.unit_len(u % st.W);
+  for (int u = wave; u < n_units; u += NW) n_steps += st.unit_len(u % st.W);
   const int n_rounds = (n_steps + P - 1) / P;
   Cursor cc = st.start(wave);
   for (int r = 1; r < n_rounds; ++r) {
@@ -629,7 +640,7 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
   // ---- partial row sums of every unit -> y, splits added in order ----
   __syncthreads();
   const int rows = (t1 - t0) * 16;
-  for (int t = threadIdx.x; t < rows * B; t += kThreads) {
+  for (int t = tid; t < rows * B; t += NT) {
     const int rl = t / B, b = t - rl * B;
     const int tl = rl >> 4, jj = rl & 15;
     const int row = t0 * 16 + rl;
@@ -661,14 +672,16 @@ __global__ __launch_bounds__(kThreads) void kernel(Args a) {
 // ---------------------------------------------------------------------------
 // Fused decode stack: one persistent launch runs a sequence of grouped
 // batch-1 GEMV stages (the projections of a decoder's layers in order), with
-// a device-wide barrier between stages instead of a kernel boundary. Each
-// stage is planned exactly as its own grouped launch and its workgroups run
-// the same body, so every output has the bits of separate launches; the
-// launch's workgroups (one per CU, co-resident by cooperative launch) take
-// the stage's planned workgroups round-robin.
+// a device-wide barrier between stages instead of a kernel boundary. The
+// launch has one workgroup of 1024 threads (16 waves, as many as two
+// 512-thread launches put on a CU) per CU, co-resident by cooperative
+// launch; each stage is planned for at most one workgroup per CU and runs
+// the matrix-core GEMV body.
+constexpr int kStackThreads = 1024;
+
 struct Stage {
   Args a;
-  int grid;  // workgroups the stage was planned for
+  int grid;  // workgroups the stage was planned for (<= the launch's)
 };
 
 // A barrier wait gives up after this many polls (about a second) and sets
@@ -677,14 +690,19 @@ constexpr uint32_t kSpinLimit = 1u << 22;
 
 // sync[0]: arrivals (target = workgroups x barriers passed), sync[1]: error.
 // What crosses stages (each stage's y, the next stages' x) is stored and
-// loaded with system-coherent accesses (the body's XC mode), so the barrier
-// needs no cache writeback or invalidation: every thread waits until its
-// stores have completed, then one thread per group arrives (device-scope
-// atomic) and polls the count.
+// loaded with system-coherent buffer accesses (sc0 sc1: write-through to
+// memory, and loads that miss every cache), so no cache needs a writeback
+// or invalidation: a thread's stores are visible to every CU once they have
+// completed, and a load issued after the barrier reads memory. Before
+// arriving, every thread waits until its stores have completed (vmcnt 0).
+// One thread per workgroup then adds one to a device-scope counter and polls
+// it (sleeping between polls); the workgroup barrier after the poll releases
+// the others.
 __device__ inline void grid_sync(uint32_t *sync, uint32_t target) {
-  __builtin_amdgcn_s_waitcnt(0);           // this thread's stores completed
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);  // no compiler motion across
-  __syncthreads();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
   if (threadIdx.x == 0) {
     __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t n = 0;
@@ -697,19 +715,16 @@ __device__ inline void grid_sync(uint32_t *sync, uint32_t target) {
     }
   }
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __syncthreads();
+  __builtin_amdgcn_s_barrier();
 }
 
-__global__ __launch_bounds__(kThreads) void stack_kernel(const Stage *stages, int n_stages,
-                                                         uint32_t *sync) {
+__global__ __launch_bounds__(kStackThreads) void stack_kernel(const Stage *__restrict__ stages, int n_stages,
+                                                              uint32_t *sync) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int vb = (int)blockIdx.x;  // this workgroup's share of every stage
   for (int s = 0; s < n_stages; ++s) {
-    const Stage &st = stages[s];
-    const int grid = st.grid;
-    for (int vb = (int)blockIdx.x; vb < grid; vb += (int)gridDim.x) {
-      body<1, 3, true, true>(st.a, vb, lds);
-      if (vb + (int)gridDim.x < grid) __syncthreads();  // LDS reused by the next block
-    }
+    if (vb < stages[s].grid) body<1, 3, true, true, false, kStackThreads>(stages[s].a, vb, lds);
+    __syncthreads();  // LDS is reused by the next stage
     grid_sync(sync, (uint32_t)(s + 1) * gridDim.x);
   }
 }
@@ -761,14 +776,14 @@ qw_status launch_b(const Args &a, int B, bool deep, int grid, size_t lds, hipStr
 }
 
 // Waves per tile: a divisor of the super-chunk count minimising the time of
-// the busiest wave of a workgroup holding `tw` tiles.
-int pick_splits(int tw, int sc) {
+// the busiest wave of a workgroup of nw waves holding `tw` tiles.
+int pick_splits(int tw, int sc, int nw) {
   int best = 1;
   long best_t = -1;
   for (int w = 1; w <= sc; ++w) {
     if (sc % w) continue;
     const long units = (long)tw * w;
-    const long t = ((units + kWaves - 1) / kWaves) * (sc / w);
+    const long t = ((units + nw - 1) / nw) * (sc / w);
     if (best_t < 0 || t < best_t) {
       best_t = t;
       best = w;
@@ -784,7 +799,7 @@ int pick_splits(int tw, int sc) {
 // workgroups wanted than ``budget``, the group's matrices share the budget
 // in proportion to their tiles (a matrix alone is never cut).
 static qw_status plan(const qw_weight *ws, int count, const uint16_t *x, void *const *ys, bool f32,
-                      int cus, Args &a, int &grid, int budget = 1 << 30) {
+                      int cus, Args &a, int &grid, int budget = 1 << 30, int nt = kThreads) {
   const int K = ws[0].K;
   if (K % 512 != 0 || count > kMats) return QW_ERR_UNSUPPORTED;
   int na_max = 0;
@@ -794,6 +809,8 @@ static qw_status plan(const qw_weight *ws, int count, const uint16_t *x, void *c
     na_max = max(na_max, (npad + kAnchorChunk - 1) / kAnchorChunk);
   }
   const int xo_len = na_max * kAnchorChunk;
+  // the body gathers up to kIdxItems * kThreads anchors (per thread scaled
+  // to the workgroup size)
   if (xo_len > kIdxItems * kThreads) return QW_ERR_UNSUPPORTED;
   const int SC = K / 512;
   a = Args{};
@@ -837,7 +854,7 @@ static qw_status plan(const qw_weight *ws, int count, const uint16_t *x, void *c
     m.wg_begin = grid;
     grid += m.wg_count;
     const int tw = (m.tiles + m.wg_count - 1) / m.wg_count;
-    m.W = pick_splits(tw, SC);
+    m.W = pick_splits(tw, SC, nt / 64);
     units_max = max(units_max, tw * m.W);
   }
   a.units_max = units_max;
@@ -1122,14 +1139,16 @@ qw_status qw_stack_prepare(const qw_stack_stage *stages, int n_stages, void *pla
     }
     int grid = 0;
     QW_TRY(qw::gemv2m::plan(sg.w, sg.count, reinterpret_cast<const uint16_t *>(sg.x), sg.y, sg.y_dtype == QW_DT_F32,
-                cus, host[i].a, grid, cus));
+                cus, host[i].a, grid, cus, kStackThreads));
+    host[i].a.xraw = 0;  // anchors gathered from global x
     const int K = sg.w[0].K;
     if ((long)K > (long)kXItems * kThreads * 8) return QW_ERR_UNSUPPORTED;
-    const size_t lds = lds_layout(1, K, host[i].a.xo_len, host[i].a.units_max).total;
+    const size_t lds = lds_layout(1, K, host[i].a.xo_len, host[i].a.units_max, 0).total;
     if (lds > 160 * 1024) return QW_ERR_UNSUPPORTED;
     lds_max = max(lds_max, lds);
     host[i].grid = grid;
   }
+
   QW_HIP_TRY(hipMemcpy(plan, host.data(), host.size() * sizeof(Stage), hipMemcpyHostToDevice));
   out->plan = plan;
   out->n_stages = n_stages;
@@ -1157,7 +1176,7 @@ qw_status qw_stack_run(const qw_stack *st, uint32_t *sync, void *stream) {
   uint32_t *sync_p = sync;
   void *args[] = {(void *)&plan_p, (void *)&n, (void *)&sync_p};
   // cooperative: every workgroup resident at once, or the launch fails
-  QW_HIP_TRY(launch_cooperative_raw(fn, dim3(st->grid), dim3(kThreads), args, (size_t)st->lds, s));
+  QW_HIP_TRY(launch_cooperative_raw(fn, dim3(st->grid), dim3(kStackThreads), args, (size_t)st->lds, s));
   return QW_OK;
 }
 

@@ -90,6 +90,10 @@ def lib():
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing; build it with "
                            "`python -m bit_weight_quantized_qw_amd.build`")
+    # torch ships its own HIP runtime: load it first, so libqw binds to that
+    # same runtime (loaded the other way round, the process would hold two
+    # runtimes and the library would see no current device)
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     c_i, c_d, c_p, c_sz = ctypes.c_int, ctypes.c_double, ctypes.c_void_p, ctypes.c_size_t
     W = ctypes.POINTER(qw_weight)

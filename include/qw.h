@@ -388,9 +388,11 @@ qw_status qgemv_2bit_grouped(const qw_weight *ws, int count, const void *x,
  * order) run by ONE persistent launch, with a device-wide barrier between
  * consecutive stages in place of a kernel boundary, so a stage starts only
  * after every output of the one before is written and visible. Each stage
- * computes exactly what qgemv_2bit_grouped computes for it on the
- * matrix-core path (same plan, same summation order: the same bits); the
- * attention and activation steps between projections are not part of it.
+ * computes what qgemv_2bit_grouped computes for it (the matrix-core GEMV's
+ * arithmetic with fp32 accumulation; the persistent launch splits the work
+ * its own way, so the last bits can differ from a separate call, and are
+ * the same from run to run); the attention and activation steps between
+ * projections are not part of it.
  * Intended for decode loops where the per-launch cost of hundreds of small
  * GEMVs per token dominates ("Key v4.0 Innovations" and section 1 of the
  * OTF-LLM page: decoding is bound by streaming every weight once per
@@ -427,8 +429,8 @@ qw_status qw_stack_prepare(const qw_stack_stage *stages, int n_stages, void *pla
                            qw_stack *out);
 
 /* Enqueues one run of a prepared stack on ``stream``: a fill kernel clears
- * sync, then one cooperative launch with one workgroup per CU runs all
- * stages.
+ * sync, then one cooperative launch with one workgroup of 1024 threads per
+ * CU runs all stages.
  *   sync  device uint32 [2] scratch owned by the caller (16-byte aligned):
  *         sync[0] counts barrier arrivals; sync[1] is non-zero after the run
  *         if a barrier wait gave up (about a second per wait; the outputs are

@@ -7,6 +7,11 @@ import oracle
 # Normwise relative error bound for the products (fp32 accumulation, fp16 or
 # fp32 output): max |y - ref| / max |ref| <= 1e-3.
 TOL = 1e-3
+# Regression bound for fp32-output decode GEMVs: the fp32 accumulation alone
+# leaves about 1e-5 normwise (measured up to 6e-6 on the 2-bit kernels and
+# 1e-7 on NF4/INT4), so a change that loses precision shows here long
+# before it reaches TOL.
+TOL_F32_GEMV = 5e-5
 
 
 def norm_err(y, ref):
