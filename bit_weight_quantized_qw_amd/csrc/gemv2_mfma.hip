@@ -684,34 +684,55 @@ struct Stage {
   int grid;  // workgroups the stage was planned for (<= the launch's)
 };
 
-// A barrier wait gives up after this many polls (about a second) and sets
-// the error word instead of hanging; the results are then invalid.
-constexpr uint32_t kSpinLimit = 1u << 22;
+// A barrier wait gives up after this many polls (a quarter of a second or
+// more) and sets the error word instead of hanging; the results are then
+// invalid, and every later wait of the run returns at once.
+constexpr uint32_t kSpinLimit = 1u << 18;
 
-// sync[0]: arrivals (target = workgroups x barriers passed), sync[1]: error.
-// What crosses stages (each stage's y, the next stages' x) is stored and
-// loaded with system-coherent buffer accesses (sc0 sc1: write-through to
-// memory, and loads that miss every cache), so no cache needs a writeback
-// or invalidation: a thread's stores are visible to every CU once they have
-// completed, and a load issued after the barrier reads memory. Before
-// arriving, every thread waits until its stores have completed (vmcnt 0).
-// One thread per workgroup then adds one to a device-scope counter and polls
-// it (sleeping between polls); the workgroup barrier after the poll releases
-// the others.
-__device__ inline void grid_sync(uint32_t *sync, uint32_t target) {
+// Sync buffer (uint32): [0] error word, [1..15] unused, [16 + w] the arrival
+// flag of workgroup w: the number of barriers it has passed in this run.
+constexpr int kSyncFlags = 16;
+
+// Device-wide barrier number `gen` (1, 2, ...) of a run. What crosses stages
+// (each stage's y, the next stages' x) is stored and loaded with
+// system-coherent buffer accesses (sc0 sc1: write-through to memory, and
+// loads that miss every cache), so no cache needs a writeback or
+// invalidation: a store is visible to every CU once it has completed, and a
+// load issued after the barrier reads memory. Arrival: every thread waits
+// until its stores have completed (vmcnt 0), the workgroup synchronizes,
+// and one thread stores gen into the workgroup's own flag (a coherent
+// store; no two workgroups write the same word, so nothing contends on a
+// counter). Wait: wave 0 reads all flags, 64 lanes times four words per
+// poll (coalesced), until every flag holds gen or more; the workgroup
+// barrier after it releases the other waves.
+__device__ inline void grid_sync(uint32_t *sync, uint32_t gen, int n_wg) {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_barrier();
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const auto rf = rsrc(sync + kSyncFlags, (uint32_t)n_wg * 4u);
+  if (threadIdx.x == 0)
+    __builtin_amdgcn_raw_buffer_store_b32(gen, rf, (int)(blockIdx.x * 4u), 0, kCoherent);
+  if (threadIdx.x < 64) {
+    const uint32_t lane = threadIdx.x;
+    const auto re = rsrc(sync, 4u);
     uint32_t n = 0;
-    while (__hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(2);
+    for (;;) {
+      // after a timed-out wait (error word set) the run only drains
+      const bool err = __builtin_amdgcn_raw_buffer_load_b32(re, 0, 0, kCoherent) != 0u;
+      bool arrived = true;  // this lane's flags
+      for (int i = 0; i < n_wg; i += 64) {  // uniform trip count
+        // flags past n_wg read as 0 through the descriptor: count them as in
+        const uint32_t f = __builtin_amdgcn_raw_buffer_load_b32(rf, (int)((i + lane) * 4u), 0, kCoherent);
+        arrived = arrived && (f >= gen || i + (int)lane >= n_wg);
+      }
+      if (__builtin_amdgcn_ballot_w64(!(err || arrived)) == 0) break;  // wave-uniform exit
       if (++n >= kSpinLimit) {
-        __hip_atomic_fetch_or(sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0)
+          __builtin_amdgcn_raw_buffer_store_b32(1u, rsrc(sync, 4u), 0, 0, kCoherent);
         break;
       }
+      __builtin_amdgcn_s_sleep(1);
     }
   }
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -725,12 +746,12 @@ __global__ __launch_bounds__(kStackThreads) void stack_kernel(const Stage *__res
   for (int s = 0; s < n_stages; ++s) {
     if (vb < stages[s].grid) body<1, 3, true, true, false, kStackThreads>(stages[s].a, vb, lds);
     __syncthreads();  // LDS is reused by the next stage
-    grid_sync(sync, (uint32_t)(s + 1) * gridDim.x);
+    grid_sync(sync, (uint32_t)(s + 1), (int)gridDim.x);
   }
 }
 
-__global__ void sync_reset_kernel(uint32_t *sync) {
-  if (threadIdx.x < 2) sync[threadIdx.x] = 0u;
+__global__ void sync_reset_kernel(uint32_t *sync, int words) {
+  for (int i = threadIdx.x; i < words; i += blockDim.x) sync[i] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -1113,6 +1134,11 @@ qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void 
 // ---------------------------------------------------------------------------
 extern "C" {
 
+size_t qw_stack_sync_bytes(const qw_stack *st) {
+  if (!st || st->grid < 1) return 0;
+  return (size_t)(qw::gemv2m::kSyncFlags + st->grid) * sizeof(uint32_t);
+}
+
 size_t qw_stack_plan_bytes(int n_stages) {
   if (n_stages < 1 || n_stages > QW_STACK_MAX_STAGES) return 0;
   return (size_t)n_stages * sizeof(qw::gemv2m::Stage);
@@ -1170,7 +1196,7 @@ qw_status qw_stack_run(const qw_stack *st, uint32_t *sync, void *stream) {
   hipStream_t s = as_stream(stream);
   const void *fn = reinterpret_cast<const void *>(&stack_kernel);
   if (st->lds > 64 * 1024) QW_HIP_TRY(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, st->lds));
-  QW_HIP_TRY(launch(sync_reset_kernel, 1, 64, 0, s, sync));
+  QW_HIP_TRY(launch(sync_reset_kernel, 1, 256, 0, s, sync, kSyncFlags + st->grid));
   const Stage *plan_p = reinterpret_cast<const Stage *>(st->plan);
   int n = st->n_stages;
   uint32_t *sync_p = sync;

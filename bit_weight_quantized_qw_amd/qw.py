@@ -30,7 +30,7 @@ EXPORTS = [
     "qw_codebook_2bit", "qw_nf4_levels", "qw_select_workspace_bytes", "qw_select_outliers",
     "qw_select_perm", "qw_permute_cols", "qw_pack",
     "qw_pack_ex", "qw_profile_accumulate", "qw_select_outliers_ex",
-    "qw_stack_plan_bytes", "qw_stack_prepare", "qw_stack_run",
+    "qw_stack_plan_bytes", "qw_stack_prepare", "qw_stack_sync_bytes", "qw_stack_run",
     "qgemv_2bit", "qgemv_2bit_workspace_bytes", "qgemv_2bit_ws", "qgemv_2bit_static", "qgemv_nf4", "qgemv_int4",
     "qgemv_2bit_grouped",
     "qgemm_prefill", "qw_tune_set", "qw_tune_get",
@@ -116,6 +116,7 @@ def lib():
                                         c_sz, c_p]),
         "qw_stack_plan_bytes": (c_sz, [c_i]),
         "qw_stack_prepare": (c_i, [ctypes.POINTER(qw_stack_stage), c_i, c_p, ctypes.POINTER(qw_stack)]),
+        "qw_stack_sync_bytes": (c_sz, [ctypes.POINTER(qw_stack)]),
         "qw_stack_run": (c_i, [ctypes.POINTER(qw_stack), c_p, c_p]),
         "qgemv_2bit": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
         "qgemv_2bit_workspace_bytes": (c_i, [W, c_i, ctypes.POINTER(c_sz)]),
@@ -616,9 +617,10 @@ class Stack:
         if nb == 0:
             raise ValueError("too many stages")
         self.plan = torch.empty(nb, dtype=torch.uint8, device="cuda")
-        self.sync = torch.zeros(4, dtype=torch.int32, device="cuda")
         self.handle = qw_stack()
         _check(lib().qw_stack_prepare(arr, n, _ptr(self.plan), ctypes.byref(self.handle)), "qw_stack_prepare")
+        sb = int(lib().qw_stack_sync_bytes(ctypes.byref(self.handle)))
+        self.sync = torch.zeros(sb // 4, dtype=torch.int32, device="cuda")
 
     def run(self):
         """Enqueue one run of every stage on the current stream."""
@@ -626,4 +628,4 @@ class Stack:
 
     def error(self):
         """Non-zero when a barrier wait of the last run gave up (synchronizes)."""
-        return int(self.sync[1].item())
+        return int(self.sync[0].item())

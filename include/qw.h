@@ -428,13 +428,19 @@ size_t qw_stack_plan_bytes(int n_stages);
 qw_status qw_stack_prepare(const qw_stack_stage *stages, int n_stages, void *plan,
                            qw_stack *out);
 
+/* Bytes of the sync buffer qw_stack_run needs for a prepared stack (0 for a
+ * NULL or unprepared handle): 16 words plus one arrival flag per workgroup
+ * of the persistent launch. Host only. */
+size_t qw_stack_sync_bytes(const qw_stack *st);
+
 /* Enqueues one run of a prepared stack on ``stream``: a fill kernel clears
  * sync, then one cooperative launch with one workgroup of 1024 threads per
  * CU runs all stages.
- *   sync  device uint32 [2] scratch owned by the caller (16-byte aligned):
- *         sync[0] counts barrier arrivals; sync[1] is non-zero after the run
- *         if a barrier wait gave up (about a second per wait; the outputs are
- *         then invalid). Runs that share a sync buffer must not overlap.
+ *   sync  device uint32 scratch of qw_stack_sync_bytes(st) bytes, owned by
+ *         the caller (16-byte aligned): word 0 is non-zero after the run if
+ *         a barrier wait gave up (a second or more per wait; the outputs
+ *         are then invalid); the rest holds the workgroups' arrival flags.
+ *         Runs that share a sync buffer must not overlap.
  * Errors: INVALID_ARG (also a handle prepared on a device with another CU
  * count), ALIGNMENT, HIP (including a cooperative launch the device
  * refuses). */
