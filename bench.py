@@ -7,7 +7,8 @@ Prints ONE JSON line. A step is one pass of the hot path over one batch of
 synthetic input for the chosen workload:
 
   decode32b_stack (default) -- one token through the 448 projection GEMVs of
-      a 64-layer 32B-shaped decoder (q/k/v and gate/up grouped per launch),
+      a 64-layer 32B-shaped decoder (q/k/v grouped per launch; gate and up as
+      one merged matrix whose launch writes silu(gate) * up, read by down),
       2-bit G32 with 3.5% fp16 anchors, 13.9 GB of weights per token. The
       line also carries a ``prefill`` object: the 70B-shaped 2-bit prefill
       GEMM (2048x8192 bf16 times 28672x8192) timed in the same run, so both
@@ -332,14 +333,19 @@ class Decode14bInt4(Workload):
 
 
 class Decode32bStack(Workload):
-    """64 layers x {qkv (grouped), o, gate+up (grouped), down}, batch 1.
-    One token is 256 launches against distinct per-layer weights."""
+    """64 layers x {qkv (grouped), o, gate/up with the gated activation,
+    down}, batch 1. One token is 256 launches against distinct per-layer
+    weights. The gate and up projections are one merged 55296 x 5120 matrix
+    whose launch writes silu(gate) * up, and the down projection reads that
+    output (the MLP half of each layer is chained as in decoding); q/k/v, o
+    and gate/up read fixed per-layer inputs (attention is not part of the
+    library)."""
     name = "decode32b_stack"
     steps, warmup = 50, 5
     L, H, I, KV = 64, 5120, 27648, 1024
+    # (name, N, K, profile/input index); "gateup" is the merged gate/up matrix
     PROJ = [("q", 5120, 5120, 0), ("k", 1024, 5120, 0), ("v", 1024, 5120, 0),
-            ("o", 5120, 5120, 1), ("gate", 27648, 5120, 2), ("up", 27648, 5120, 2),
-            ("down", 5120, 27648, 3)]
+            ("o", 5120, 5120, 1), ("gateup", 55296, 5120, 2), ("down", 5120, 27648, 3)]
 
     def __init__(self, layers=None):
         import torch
@@ -372,8 +378,7 @@ class Decode32bStack(Workload):
         self.yk = torch.empty((1, 1024), dtype=torch.float16, device="cuda")
         self.yv = torch.empty((1, 1024), dtype=torch.float16, device="cuda")
         self.yo = torch.empty((1, 5120), dtype=torch.float16, device="cuda")
-        self.yg = torch.empty((1, 27648), dtype=torch.float16, device="cuda")
-        self.yu = torch.empty((1, 27648), dtype=torch.float16, device="cuda")
+        self.yact = torch.empty((1, 27648), dtype=torch.float16, device="cuda")  # silu(gate) * up
         self.yd = torch.empty((1, 5120), dtype=torch.float16, device="cuda")
 
     def launches(self, i):
@@ -385,9 +390,8 @@ class Decode32bStack(Workload):
                 ("qkv", lambda d=d, x=x: qw.qgemv_2bit_grouped([d["q"], d["k"], d["v"]], x[0][:, :self.H],
                                                                outs=[self.yq, self.yk, self.yv])),
                 ("o", lambda d=d, x=x: qw.qgemv_2bit(d["o"], x[1][:, :self.H], out=self.yo)),
-                ("gateup", lambda d=d, x=x: qw.qgemv_2bit_grouped([d["gate"], d["up"]], x[2][:, :self.H],
-                                                                  outs=[self.yg, self.yu])),
-                ("down", lambda d=d, x=x: qw.qgemv_2bit(d["down"], x[3][:, :self.I], out=self.yd)),
+                ("gateup", lambda d=d, x=x: qw.qgemv_2bit_swiglu(d["gateup"], x[2][:, :self.H], out=self.yact)),
+                ("down", lambda d=d: qw.qgemv_2bit(d["down"], self.yact, out=self.yd)),
             ]
         return out
 
@@ -397,7 +401,7 @@ class Decode32bStack(Workload):
         nb = lambda p: _gemv2_bytes(p.N, p.K, p.n_out, 1)
         b["qkv"] = nb(d["q"]) + nb(d["k"]) + nb(d["v"]) - 2 * 2 * 5120
         b["o"] = nb(d["o"])
-        b["gateup"] = nb(d["gate"]) + nb(d["up"]) - 2 * 5120
+        b["gateup"] = nb(d["gateup"]) - self.I * 2  # I outputs, not 2I
         b["down"] = nb(d["down"])
         return b
 
@@ -407,7 +411,8 @@ class Decode32bStack(Workload):
     def config(self):
         return {"workload": self.name, "layers": self.L, "hidden": self.H, "intermediate": self.I,
                 "heads": "40q/8kv x 128", "batch": 1, "anchor_frac": 0.035,
-                "formats": ["2bit_g32"], "launches_per_token": 4 * self.L}
+                "formats": ["2bit_g32"], "mlp": "merged gate/up GEMV writes silu(gate)*up; down reads it",
+                "launches_per_token": 4 * self.L}
 
     def cpu_baseline(self):
         import oracle
@@ -419,21 +424,26 @@ class Decode32bStack(Workload):
             X = inputs.profile(256, K, workload=4, layer=0, proj=inp)
             idx = oracle.select_outliers(W, X, 0.035)
             rows = N // frac_rows
-            r = oracle.quantize_2bit(W[:rows], idx)
+            sel = np.arange(rows)
+            if nm == "gateup":  # gate rows and the up rows they pair with
+                sel = np.concatenate([np.arange(rows // 2), N // 2 + np.arange(rows // 2)])
+            r = oracle.quantize_2bit(W[sel], idx)
             x = inputs.act_f16(1, K, workload=4, layer=0, proj=p)
-            jobs.append((x, oracle.pack_2bit(r["q"]), r))
+            jobs.append((nm == "gateup", x, oracle.pack_2bit(r["q"]), r))
             amount += _gemv2_bytes(rows, K, len(idx), 1)
 
         def one():
-            for x, c, r in jobs:
-                oracle.gemv_2bit_ref(x, oracle.unpack_2bit(c), r["S"], r["Z"], r["idx"], r["W_O"])
-        return _time_oracle(one, amount, "layer 0, first 1/8 of the rows of each of the 7 projections")
+            for sw, x, c, r in jobs:
+                f = oracle.gemv_2bit_swiglu_ref if sw else oracle.gemv_2bit_ref
+                f(x, oracle.unpack_2bit(c), r["S"], r["Z"], r["idx"], r["W_O"])
+        return _time_oracle(one, amount, "layer 0, 1/8 of the rows of each of the 6 matrices "
+                                         "(gate/up: the first 1/16 of each half, with the activation)")
 
 
 class Decode32bStackFused(Decode32bStack):
-    """The same token (same weights, inputs and the 448 products) as one
-    persistent launch: the 256 stages run in order with a device-wide barrier
-    between consecutive stages (qw_stack_run)."""
+    """The same token (same weights, inputs, the 448 products and the gated
+    activation) as one persistent launch: the 256 stages run in order with a
+    device-wide barrier between consecutive stages (qw_stack_run)."""
     name = "decode32b_stack_fused"
     graph = False  # one launch per token already
 
@@ -447,8 +457,8 @@ class Decode32bStackFused(Decode32bStack):
             stages += [
                 ([d["q"], d["k"], d["v"]], x[0][0, :self.H], [self.yq[0], self.yk[0], self.yv[0]]),
                 ([d["o"]], x[1][0, :self.H], [self.yo[0]]),
-                ([d["gate"], d["up"]], x[2][0, :self.H], [self.yg[0], self.yu[0]]),
-                ([d["down"]], x[3][0, :self.I], [self.yd[0]]),
+                ([d["gateup"]], x[2][0, :self.H], [self.yact[0]], True),
+                ([d["down"]], self.yact[0], [self.yd[0]]),
             ]
         self.stack = qw.Stack(stages)
         log(f"stack: {len(stages)} stages planned, {self.stack.handle.lds} B LDS per workgroup")

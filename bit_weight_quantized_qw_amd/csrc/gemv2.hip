@@ -15,6 +15,8 @@ namespace gemv2m {
 qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void *const *ys,
                  bool f32, int cus, float *work, size_t work_bytes, hipStream_t s);
 size_t split_workspace_bytes(const qw_weight &w, int B, int cus);
+qw_status launch_swiglu(const qw_weight &w, const uint16_t *x, int B, void *y, bool f32, int cus,
+                        hipStream_t s);
 }  // namespace gemv2m
 
 namespace gemv2 {
@@ -271,6 +273,21 @@ qw_status qgemv_2bit_static(const qw_weight *w, const void *x, int B, void *y, q
   if (need > 0) QW_TRY(static_scratch(&ws));
   void *ys[1] = {y};
   return gemv2::launch(w, 1, x, B, ys, y_dtype, ws, need, as_stream(stream));
+}
+
+qw_status qgemv_2bit_swiglu(const qw_weight *w, const void *x, int B, void *y, qw_dtype y_dtype,
+                            void *stream) {
+  using namespace qw;
+  CallScope scope;
+  QW_TRY(gemv2::check_args(w, 1, B));
+  if (!x || !y) return QW_ERR_INVALID_ARG;
+  if (y_dtype != QW_DT_F16 && y_dtype != QW_DT_F32) return QW_ERR_INVALID_ARG;
+  if (w->N % 32 != 0) return QW_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y)) return QW_ERR_ALIGNMENT;
+  int cus = 0;
+  QW_TRY(current_device(&cus));
+  return gemv2m::launch_swiglu(*w, reinterpret_cast<const uint16_t *>(x), B, y, y_dtype == QW_DT_F32, cus,
+                               as_stream(stream));
 }
 
 qw_status qgemv_2bit_grouped(const qw_weight *ws, int count, const void *x, int B,

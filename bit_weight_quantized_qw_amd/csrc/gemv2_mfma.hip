@@ -97,7 +97,13 @@ struct Args {
   int xraw;           // 1: raw x copied to LDS for the anchor gather; 0:
                       // anchors gathered from global x (frees B*(K+8)*2
                       // bytes of LDS so wider batches fit one pass)
+  int swiglu;         // 1: one merged gate/up matrix (m[0], 2I rows: gate
+                      // rows 0..I-1, up rows I..2I-1, I % 16 == 0); y gets
+                      // silu(gate) * up, I values per batch row
 };
+
+// SiLU of the gate projection's output, g * sigmoid(g), in fp32.
+__device__ inline float silu(float g) { return g / (1.0f + expf(-g)); }
 
 // LDS layout, bytes:
 //   limbs  [B][G][3][32]   e4m3 limbs per group (two 16-byte halves)
@@ -245,7 +251,11 @@ __device__ inline T sel4(int i, T v0, T v1, T v2, T v3) {
 // planned for) of a grouped GEMV, with the group's LDS at lds.
 // XR: raw x kept in LDS for the anchor gather (a.xraw == 1); false only for
 // batches that fit one pass without it. NT: threads of the workgroup.
-template <int B, int P, bool MULTI, bool XC = false, bool XR = true, int NT = kThreads>
+// SW: the merged gate/up product with the gated activation in the epilogue
+// (a.swiglu == 1, a single matrix): the workgroup's items are tile pairs, the
+// gate tile p and the up tile H + p (H = I / 16), so both factors of each of
+// its outputs meet in its own LDS.
+template <int B, int P, bool MULTI, bool XC = false, bool XR = true, int NT = kThreads, bool SW = false>
 __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds) {
   constexpr int NW = NT / 64;
   // prologue items per thread: the same totals as at kThreads threads
@@ -291,12 +301,17 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
   const int wi = bid - M.wg_begin;
   // (wi + 1) * tiles < 2^31: tiles <= 2^27 and workgroups per matrix <= 16
   // per CU of a 256-CU part are checked on the host
-  const int t0 = (int)((uint32_t)(wi * M.tiles) / (uint32_t)M.wg_count);
-  const int t1 = (int)((uint32_t)((wi + 1) * M.tiles) / (uint32_t)M.wg_count);
+  // work items: tiles, or tile pairs (SW); this workgroup's are [t0, t1)
+  const int H = SW ? M.tiles >> 1 : M.tiles;
+  const int t0 = (int)((uint32_t)(wi * H) / (uint32_t)M.wg_count);
+  const int t1 = (int)((uint32_t)((wi + 1) * H) / (uint32_t)M.wg_count);
+  const int np = t1 - t0;
   const int W = M.W;
   const int L = SC / W;
   const int NA = (M.n_out_pad + kAnchorChunk - 1) / kAnchorChunk;
-  const int n_units = (t1 - t0) * W;
+  // local tiles: [0, np) the items' tiles, and with SW [np, 2 np) their up
+  // tiles
+  const int n_units = (SW ? 2 * np : np) * W;
   const Lds lay = lds_layout(B, K, a.xo_len, a.units_max, XR ? 1 : 0);
   uint8_t *limbs = lds + lay.limbs;
   uint8_t *zero = lds + lay.zero;
@@ -328,7 +343,8 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
   // branch-free issue path: descriptor and offsets are picked per step kind.
   auto issue = [&](Slot &dst, const Cursor &c) __attribute__((always_inline)) {
     const bool live = c.unit < n_units;
-    const int tile = t0 + (live ? c.tile : 0);
+    const int lt = live ? c.tile : 0;
+    const int tile = SW ? (lt < np ? t0 + lt : H + t0 + (lt - np)) : t0 + lt;
     const int split = live ? c.split : 0;
     const bool row_ok = live && tile * 16 + j < M.N;
     const bool code = c.step < L;
@@ -639,6 +655,35 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
 
   // ---- partial row sums of every unit -> y, splits added in order ----
   __syncthreads();
+  if (SW) {
+    // gate row t0 * 16 + rl pairs with up row I + t0 * 16 + rl
+    const int I = H * 16;
+    const size_t esz = a.f32out ? 4 : 2;
+    for (int t = tid; t < np * 16 * B; t += NT) {
+      const int rl = t / B, b = t - rl * B;
+      const int tl = rl >> 4, jj = rl & 15;
+      float g = 0.0f, u = 0.0f;
+      for (int sp = 0; sp < W; ++sp) {
+        g += parts[((size_t)(tl * W + sp) * 16 + jj) * B + b];
+        u += parts[((size_t)((np + tl) * W + sp) * 16 + jj) * B + b];
+      }
+      const float v = silu(g) * u;
+      const size_t off = (size_t)b * I + t0 * 16 + rl;
+      if (XC) {
+        const auto ry = rsrc(M.y, (uint32_t)((size_t)B * I * esz));
+        if (a.f32out)
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ry, (int)(off * 4), 0, kCoherent);
+        else
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)v), ry, (int)(off * 2), 0,
+                                                kCoherent);
+      } else if (a.f32out) {
+        reinterpret_cast<float *>(M.y)[off] = v;
+      } else {
+        reinterpret_cast<_Float16 *>(M.y)[off] = (_Float16)v;
+      }
+    }
+    return;
+  }
   const int rows = (t1 - t0) * 16;
   for (int t = tid; t < rows * B; t += NT) {
     const int rl = t / B, b = t - rl * B;
@@ -663,10 +708,10 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
   }
 }
 
-template <int B, int P, bool MULTI, bool XR = true>
+template <int B, int P, bool MULTI, bool XR = true, bool SW = false>
 __global__ __launch_bounds__(kThreads) void kernel(Args a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  body<B, P, MULTI, false, XR>(a, (int)blockIdx.x, lds);
+  body<B, P, MULTI, false, XR, kThreads, SW>(a, (int)blockIdx.x, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -744,7 +789,12 @@ __global__ __launch_bounds__(kStackThreads) void stack_kernel(const Stage *__res
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int vb = (int)blockIdx.x;  // this workgroup's share of every stage
   for (int s = 0; s < n_stages; ++s) {
-    if (vb < stages[s].grid) body<1, 3, true, true, false, kStackThreads>(stages[s].a, vb, lds);
+    if (vb < stages[s].grid) {
+      if (stages[s].a.swiglu)
+        body<1, 3, false, true, false, kStackThreads, true>(stages[s].a, vb, lds);
+      else
+        body<1, 3, true, true, false, kStackThreads>(stages[s].a, vb, lds);
+    }
     __syncthreads();  // LDS is reused by the next stage
     grid_sync(sync, (uint32_t)(s + 1), (int)gridDim.x);
   }
@@ -759,13 +809,13 @@ __global__ void sync_reset_kernel(uint32_t *sync, int words) {
 
 namespace {
 
-template <int B, int P, bool MULTI, bool XR>
+template <int B, int P, bool MULTI, bool XR, bool SW = false>
 qw_status launch_bpmx(const Args &a, int grid, size_t lds, hipStream_t s) {
   if (lds > 64 * 1024) {
-    QW_HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(&kernel<B, P, MULTI, XR>),
+    QW_HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(&kernel<B, P, MULTI, XR, SW>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds));
   }
-  QW_HIP_TRY(launch(kernel<B, P, MULTI, XR>, grid, kThreads, lds, s, a));
+  QW_HIP_TRY(launch(kernel<B, P, MULTI, XR, SW>, grid, kThreads, lds, s, a));
   return QW_OK;
 }
 
@@ -779,6 +829,11 @@ qw_status launch_bpm(const Args &a, int grid, size_t lds, hipStream_t s) {
 
 template <int B, int P>
 qw_status launch_bp(const Args &a, int grid, size_t lds, hipStream_t s) {
+  if constexpr (P == 3) {  // the merged gate/up product runs on the 3-slot ring only
+    if (a.swiglu)
+      return a.xraw ? launch_bpmx<B, P, false, true, true>(a, grid, lds, s)
+                    : launch_bpmx<B, P, false, false, true>(a, grid, lds, s);
+  }
   return a.count > 1 ? launch_bpm<B, P, true>(a, grid, lds, s) : launch_bpm<B, P, false>(a, grid, lds, s);
 }
 
@@ -819,10 +874,15 @@ int pick_splits(int tw, int sc, int nw) {
 // QW_ERR_UNSUPPORTED when the shape does not fit this kernel. With more
 // workgroups wanted than ``budget``, the group's matrices share the budget
 // in proportion to their tiles (a matrix alone is never cut).
+// swiglu: ws[0] alone is a merged gate/up matrix (N = 2I, I % 16 == 0); its
+// I / 16 tile pairs are dealt to up to 2 workgroups per CU (as many as the
+// two matrices would take as a grouped launch), within ``budget``.
 static qw_status plan(const qw_weight *ws, int count, const uint16_t *x, void *const *ys, bool f32,
-                      int cus, Args &a, int &grid, int budget = 1 << 30, int nt = kThreads) {
+                      int cus, Args &a, int &grid, int budget = 1 << 30, int nt = kThreads,
+                      bool swiglu = false) {
   const int K = ws[0].K;
   if (K % 512 != 0 || count > kMats) return QW_ERR_UNSUPPORTED;
+  if (swiglu && (count != 1 || ws[0].N % 32 != 0)) return QW_ERR_INVALID_ARG;
   int na_max = 0;
   for (int i = 0; i < count; ++i) {
     const int npad = ws[i].n_out > 0 ? ws[i].n_out_pad : 0;
@@ -842,6 +902,7 @@ static qw_status plan(const qw_weight *ws, int count, const uint16_t *x, void *c
   a.f32out = f32 ? 1 : 0;
   a.xo_len = xo_len;
   a.xraw = 1;
+  a.swiglu = swiglu ? 1 : 0;
   // every matrix is planned as if it were launched alone (its workgroup
   // count, hence its K split and summation order, do not depend on what it
   // is grouped with), so a grouped launch gives the bits of separate ones
@@ -860,7 +921,7 @@ static qw_status plan(const qw_weight *ws, int count, const uint16_t *x, void *c
     m.n_out_pad = ws[i].n_out > 0 ? ws[i].n_out_pad : 0;
     m.ld_a = m.n_out_pad;
     m.tiles = (m.N + 15) / 16;
-    m.wg_count = max(1, min(m.tiles, cus));
+    m.wg_count = swiglu ? max(1, min(m.tiles / 2, min(2 * cus, budget))) : max(1, min(m.tiles, cus));
   }
   long want = 0, all_tiles = 0;
   for (int i = 0; i < count; ++i) {
@@ -874,7 +935,9 @@ static qw_status plan(const qw_weight *ws, int count, const uint16_t *x, void *c
     Mat &m = a.m[i];
     m.wg_begin = grid;
     grid += m.wg_count;
-    const int tw = (m.tiles + m.wg_count - 1) / m.wg_count;
+    // tiles of the busiest workgroup (two per pair with swiglu)
+    const int tw = swiglu ? 2 * ((m.tiles / 2 + m.wg_count - 1) / m.wg_count)
+                          : (m.tiles + m.wg_count - 1) / m.wg_count;
     m.W = pick_splits(tw, SC, nt / 64);
     units_max = max(units_max, tw * m.W);
   }
@@ -1128,6 +1191,36 @@ qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void 
   return QW_OK;
 }
 
+// The merged gate/up product with the gated activation (y: [B][N / 2]):
+// unsplit launches only, in balanced batch slices as above. Returns
+// QW_ERR_UNSUPPORTED when no slice of two or more rows, nor of one, fits.
+qw_status launch_swiglu(const qw_weight &w, const uint16_t *x, int B, void *y, bool f32, int cus,
+                        hipStream_t s) {
+  if (B < 1 || B > 8) return QW_ERR_UNSUPPORTED;
+  const int K = w.K;
+  Args a;
+  int grid = 0;
+  void *ys[1] = {y};
+  QW_TRY(plan(&w, 1, x, ys, f32, cus, a, grid, 1 << 30, kThreads, true));
+  int xr = 1, bmax = 0;
+  int n_slices = unsplit_slices(a, B, &xr, &bmax);
+  if (n_slices == 0 && bmax == 1) n_slices = B;  // one row at a time
+  if (n_slices == 0) return QW_ERR_UNSUPPORTED;
+  a.xraw = xr;
+  const size_t esz = f32 ? 4 : 2;
+  int b0 = 0;
+  for (int sl = 0; sl < n_slices; ++sl) {
+    const int bs = (B - b0 + (n_slices - sl) - 1) / (n_slices - sl);
+    Args as = a;
+    as.x = x + (size_t)b0 * K;
+    as.m[0].y = reinterpret_cast<char *>(y) + (size_t)b0 * (w.N / 2) * esz;
+    const size_t lds = lds_layout(bs, K, a.xo_len, a.units_max, a.xraw).total;
+    QW_TRY(launch_b(as, bs, false, grid, lds, s));
+    b0 += bs;
+  }
+  return QW_OK;
+}
+
 }  // namespace gemv2m
 }  // namespace qw
 
@@ -1156,6 +1249,8 @@ qw_status qw_stack_prepare(const qw_stack_stage *stages, int n_stages, void *pla
   for (int i = 0; i < n_stages; ++i) {
     const qw_stack_stage &sg = stages[i];
     if (sg.count < 1 || sg.count > kMats || !sg.x) return QW_ERR_INVALID_ARG;
+    if (sg.swiglu != 0 && sg.swiglu != 1) return QW_ERR_INVALID_ARG;
+    if (sg.swiglu && (sg.count != 1 || sg.w[0].N % 32 != 0)) return QW_ERR_INVALID_ARG;
     if (sg.y_dtype != QW_DT_F16 && sg.y_dtype != QW_DT_F32) return QW_ERR_INVALID_ARG;
     if (!aligned16(sg.x)) return QW_ERR_ALIGNMENT;
     for (int m = 0; m < sg.count; ++m) {
@@ -1165,7 +1260,7 @@ qw_status qw_stack_prepare(const qw_stack_stage *stages, int n_stages, void *pla
     }
     int grid = 0;
     QW_TRY(qw::gemv2m::plan(sg.w, sg.count, reinterpret_cast<const uint16_t *>(sg.x), sg.y, sg.y_dtype == QW_DT_F32,
-                cus, host[i].a, grid, cus, kStackThreads));
+                cus, host[i].a, grid, cus, kStackThreads, sg.swiglu != 0));
     host[i].a.xraw = 0;  // anchors gathered from global x
     const int K = sg.w[0].K;
     if ((long)K > (long)kXItems * kThreads * 8) return QW_ERR_UNSUPPORTED;

@@ -32,7 +32,7 @@ EXPORTS = [
     "qw_pack_ex", "qw_profile_accumulate", "qw_select_outliers_ex",
     "qw_stack_plan_bytes", "qw_stack_prepare", "qw_stack_sync_bytes", "qw_stack_run",
     "qgemv_2bit", "qgemv_2bit_workspace_bytes", "qgemv_2bit_ws", "qgemv_2bit_static", "qgemv_nf4", "qgemv_int4",
-    "qgemv_2bit_grouped",
+    "qgemv_2bit_grouped", "qgemv_2bit_swiglu",
     "qgemm_prefill", "qw_tune_set", "qw_tune_get",
 ]
 
@@ -68,7 +68,7 @@ class qw_sizes(ctypes.Structure):
 class qw_stack_stage(ctypes.Structure):
     _fields_ = [
         ("count", ctypes.c_int32), ("w", qw_weight * 4), ("x", ctypes.c_void_p),
-        ("y", ctypes.c_void_p * 4), ("y_dtype", ctypes.c_int32),
+        ("y", ctypes.c_void_p * 4), ("y_dtype", ctypes.c_int32), ("swiglu", ctypes.c_int32),
     ]
 
 
@@ -125,6 +125,7 @@ def lib():
         "qgemv_nf4": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
         "qgemv_int4": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
         "qgemv_2bit_grouped": (c_i, [W, c_i, c_p, c_i, ctypes.POINTER(c_p), c_i, c_p]),
+        "qgemv_2bit_swiglu": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
         "qgemm_prefill": (c_i, [W, c_p, c_i, c_p, c_i, c_p]),
         "qw_tune_set": (c_i, [c_i, c_i]),
         "qw_tune_get": (c_i, [c_i]),
@@ -566,6 +567,23 @@ def qgemv_2bit_grouped(pws, x, out_dtype=None, outs=None):
     return ys
 
 
+def qgemv_2bit_swiglu(pw, x, out_dtype=None, out=None):
+    """silu(gate) * up for a merged gate/up weight (gate rows over up rows,
+    N = 2I): y (B, I)."""
+    import torch
+    _need(x, torch.float16, "x", 2)
+    if pw.N % 32:
+        raise ValueError("a merged gate/up weight has N = 2I rows with I % 16 == 0")
+    out_dtype = out_dtype or torch.float16
+    B = x.shape[0]
+    y = out if out is not None else torch.empty((B, pw.N // 2), dtype=out_dtype, device=x.device)
+    _io_shapes(pw, x, [(y, pw.N // 2)])
+    v = pw.view()
+    _check(lib().qgemv_2bit_swiglu(ctypes.byref(v), _ptr(x), B, _ptr(y), _dt(y.dtype), _stream()),
+           "qgemv_2bit_swiglu")
+    return y
+
+
 def qgemm_prefill(pw, X, out_dtype=None, out=None):
     import torch
     _need(X, torch.bfloat16, "X", 2)
@@ -587,31 +605,38 @@ def qw_stack_plan_bytes(n_stages):
 
 class Stack:
     """A prepared fused decode stack (qw_stack_prepare) and its device plan
-    and sync buffers. ``stages`` is a list of (weights, x, ys): up to four
-    PackedWeight (2-bit) sharing the fp16 input x (K,) and their outputs ys
-    ((N_i,) fp16 or fp32 tensors). The tensors are referenced, not copied:
-    each run reads and writes them in place."""
+    and sync buffers. ``stages`` is a list of (weights, x, ys) or (weights,
+    x, ys, swiglu): up to four PackedWeight (2-bit) sharing the fp16 input x
+    (K,) and their outputs ys ((N_i,) fp16 or fp32 tensors); with swiglu
+    true, one merged gate/up weight (N = 2I) whose output ys[0] (I,) gets
+    silu(gate) * up. The tensors are referenced, not copied: each run reads
+    and writes them in place."""
 
     def __init__(self, stages):
         import torch
         n = len(stages)
         arr = (qw_stack_stage * n)()
         self._keep = []
-        for i, (ws, x, ys) in enumerate(stages):
+        for i, st in enumerate(stages):
+            ws, x, ys = st[:3]
+            sw = bool(st[3]) if len(st) > 3 else False
             if not 1 <= len(ws) <= 4 or len(ys) != len(ws):
                 raise ValueError("a stage has 1..4 weights and as many outputs")
+            if sw and len(ws) != 1:
+                raise ValueError("a swiglu stage has one merged gate/up weight")
             _need(x, torch.float16, "x", 1)
             dt = ys[0].dtype
             for pw, y in zip(ws, ys):
                 _need(y, dt, "y", 1)
-                if pw.K != x.numel() or pw.N != y.numel():
-                    raise ValueError("stage buffers must hold K inputs and N outputs of each weight")
+                if pw.K != x.numel() or (pw.N // 2 if sw else pw.N) != y.numel():
+                    raise ValueError("stage buffers must hold K inputs and the outputs of each weight")
             arr[i].count = len(ws)
             for m, (pw, y) in enumerate(zip(ws, ys)):
                 arr[i].w[m] = pw.view()
                 arr[i].y[m] = y.data_ptr()
             arr[i].x = x.data_ptr()
             arr[i].y_dtype = QW_DT_F32 if dt == torch.float32 else QW_DT_F16
+            arr[i].swiglu = 1 if sw else 0
             self._keep.append((ws, x, ys))
         nb = qw_stack_plan_bytes(n)
         if nb == 0:

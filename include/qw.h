@@ -383,6 +383,27 @@ qw_status qgemv_2bit_grouped(const qw_weight *ws, int count, const void *x,
                              int B, void *const *ys, qw_dtype y_dtype,
                              void *stream);
 
+/* The gate and up projections of a gated MLP block with the activation
+ * between them and the down projection, in one launch:
+ *   y[b][n] = silu(g[b][n]) * u[b][n],   silu(t) = t / (1 + exp(-t)),
+ *   g[b][n] = sum_k x[b][k] w_hat[n][k], u[b][n] = sum_k x[b][k] w_hat[I+n][k]
+ * for n < I, where w is ONE 2-bit view of N = 2I rows: the gate rows
+ * (0..I-1) stacked over the up rows (I..2I-1), packed, with its anchor
+ * channels selected, as one matrix (the two share their input). Each
+ * output's two sums are accumulated as by qgemv_2bit (fp32), the
+ * activation and the product in fp32, then one rounding to y_dtype; y is
+ * [B][I] and is the down projection's x when y_dtype is fp16. The pages do
+ * not name the activation: SiLU is the one of the decoder shapes they quote
+ * (the 32B-class block of hidden 5120 and intermediate 27648), and the
+ * fusion serves their per-token streaming argument ("On-The-Fly Weight
+ * Synthesizer (OTF-LLM Engine v4.0)", section 1: every weight is fetched
+ * once per token, so nothing else should cost a pass).
+ * Conventions as qgemv_2bit; needs no workspace. Errors: INVALID_ARG also
+ * for N not a multiple of 32; UNSUPPORTED when K % 512 != 0 or the batch's
+ * x does not fit a workgroup (no K split and no vector-ALU path here). */
+qw_status qgemv_2bit_swiglu(const qw_weight *w, const void *x, int B, void *y,
+                            qw_dtype y_dtype, void *stream);
+
 /* Fused decode stack (batch 1): a sequence of grouped 2-bit GEMV stages
  * (for example q/k/v, o, gate/up and down of every layer of a decoder, in
  * order) run by ONE persistent launch, with a device-wide barrier between
@@ -391,8 +412,10 @@ qw_status qgemv_2bit_grouped(const qw_weight *ws, int count, const void *x,
  * computes what qgemv_2bit_grouped computes for it (the matrix-core GEMV's
  * arithmetic with fp32 accumulation; the persistent launch splits the work
  * its own way, so the last bits can differ from a separate call, and are
- * the same from run to run); the attention and activation steps between
- * projections are not part of it.
+ * the same from run to run); a stage with swiglu set computes what
+ * qgemv_2bit_swiglu computes (the gated activation feeding the down
+ * projection), while the attention steps between projections are not part
+ * of it.
  * Intended for decode loops where the per-launch cost of hundreds of small
  * GEMVs per token dominates ("Key v4.0 Innovations" and section 1 of the
  * OTF-LLM page: decoding is bound by streaming every weight once per
@@ -405,6 +428,9 @@ typedef struct {
   const void *x;      /* device fp16 [K] (batch 1) */
   void *y[4];         /* device [N_i] outputs, fp16 or fp32 per y_dtype */
   int32_t y_dtype;    /* QW_DT_F16 or QW_DT_F32 */
+  int32_t swiglu;     /* 0, or 1: count is 1, w[0] is a merged gate/up view
+                         (N % 32 == 0) and y[0] gets [N/2] gated values, as
+                         qgemv_2bit_swiglu */
 } qw_stack_stage;
 
 /* Host handle of a prepared stack, written by qw_stack_prepare. */

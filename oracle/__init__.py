@@ -18,6 +18,9 @@ generators. The oracle is written from the pages that define the method:
   (v4.0)" and "Method Comparison Table": the v3.2 INT4 format (uniform
   symmetric grid, two codes per byte, a static channel permutation, the top
   1% channels in FP16).
+* the gated activation between the gate/up and down projections of the
+  decoder blocks the OTF-LLM page quantizes (``mlp``): the pages do not name
+  it; the reading (SiLU, gate and up as one merged matrix) is stated there.
 
 Where the pages leave a step open, the reading taken is stated in the
 docstring of the function that takes it. Every function here is pinned by a
@@ -51,6 +54,7 @@ from .int4perm import (GROUP_INT4, QMAX_INT4, ANCHOR_FRAC_INT4, int4_permutation
                        prefill_weight_bf16_int4)
 from .products import (gemv_2bit_ref, gemv_nf4_ref, prefill_weight_bf16_2bit,
                        prefill_weight_bf16_nf4, gemm_prefill_ref)
+from .mlp import silu, swiglu_ref, gemv_2bit_swiglu_ref
 
 __all__ = [
     "CODEBOOK_F32", "CODEBOOK", "lloyd_max_gaussian", "gaussian_msqe",
@@ -66,4 +70,5 @@ __all__ = [
     "prefill_weight_bf16_int4",
     "gemv_2bit_ref", "gemv_nf4_ref", "prefill_weight_bf16_2bit",
     "prefill_weight_bf16_nf4", "gemm_prefill_ref",
+    "silu", "swiglu_ref", "gemv_2bit_swiglu_ref",
 ]

@@ -4,7 +4,10 @@ persistent launch, with a device-wide barrier between stages. Chained stages
 (o reads y_q, down reads y_gate as the run wrote them) check cross-stage
 visibility: their reference takes its input from the oracle's own chain
 (y_q, y_gate computed by the oracle and rounded to fp16), never from the
-device. A second run gives the same bits. No barrier wait may give up."""
+device; anchors are the oracle's choice (the device's is checked equal). A
+stage with the gated activation (a merged gate/up matrix) feeds the down
+projection as a decoder block does. A second run gives the same bits. No
+barrier wait may give up."""
 
 import numpy as np
 import pytest
@@ -23,10 +26,13 @@ def _packed(N, K, seed, frac=0.035):
     W = inputs.weight(N, K, workload=seed)
     X = inputs.profile(32, K, workload=seed)
     Wd = to_dev(W)
-    idx = qw.qw_select_outliers(Wd, to_dev(X), frac) if frac else None
-    pw = qw.qw_pack(Wd, qw.QW_FMT_2BIT_G32, idx)
+    idx = oracle.select_outliers(W, X, frac) if frac else None
+    if idx is not None:
+        dev = qw.qw_select_outliers(Wd, to_dev(X), frac).cpu().numpy()
+        np.testing.assert_array_equal(np.sort(dev), np.sort(idx))
+    pw = qw.qw_pack(Wd, qw.QW_FMT_2BIT_G32, None if idx is None else to_dev(np.asarray(idx, np.int32)))
     torch.cuda.synchronize()
-    return W, pw, (None if idx is None else idx.cpu().numpy())
+    return W, pw, idx
 
 
 def _layer(l, y_dtype):
@@ -95,6 +101,50 @@ def test_stack_chained_layers_match_oracle(L):
             assert torch.equal(t, ft)
 
 
+@pytest.mark.parametrize("L", [1, 2])
+def test_stack_swiglu_feeds_down(L):
+    """Per layer: q/k/v, o (reads y_q), the merged gate/up stage writing
+    silu(gate) * up (fp16), and down reading it: the MLP half of a decoder
+    block as it runs per token."""
+    import torch
+    stages, layers = [], []
+    for l in range(L):
+        s = 300 + 10 * l
+        w = {n: _packed(N, K, s + i) for i, (n, N, K) in enumerate(
+            [("q", H, H), ("k", KV, H), ("v", KV, H), ("o", H, H), ("gateup", 2 * I, H), ("down", H, I)])}
+        x_attn = f16_dev(inputs.act_f16(1, H, workload=s)[0])
+        x_mlp = f16_dev(inputs.act_f16(1, H, workload=s + 7)[0])
+        y = {n: torch.zeros(H if n in ("q", "o", "down") else (KV if n in ("k", "v") else I),
+                            dtype=torch.float16, device="cuda") for n in w}
+        stages.append(([w["q"][1], w["k"][1], w["v"][1]], x_attn, [y["q"], y["k"], y["v"]]))
+        stages.append(([w["o"][1]], y["q"], [y["o"]]))
+        stages.append(([w["gateup"][1]], x_mlp, [y["gateup"]], True))
+        stages.append(([w["down"][1]], y["gateup"], [y["down"]]))
+        layers.append((w, x_attn, x_mlp, y))
+    st = qw.Stack(stages)
+    st.run()
+    torch.cuda.synchronize()
+    assert st.error() == 0
+    for li, (w, x_attn, x_mlp, y) in enumerate(layers):
+        xm = x_mlp.cpu().numpy()
+        Wg, _, idx = w["gateup"]
+        r = oracle.quantize_2bit(Wg, idx)
+        act = oracle.gemv_2bit_swiglu_ref(np.asarray(xm, np.float16)[None, :], r["q"], r["S"], r["Z"],
+                                          r["idx"], r["W_O"])[0]
+        ref_down = _oracle_y(w["down"], oracle.fp16_rne(act))
+        e_act = norm_err(y["gateup"].float().cpu().numpy()[None, :], act[None, :])
+        e_down = norm_err(y["down"].float().cpu().numpy()[None, :], ref_down[None, :])
+        print(f"layer {li}: silu(gate)*up err {e_act:.3e}, down err {e_down:.3e}")
+        assert e_act <= TOL and e_down <= TOL
+    first = [[t.clone() for t in ys] for _, _, ys, *_ in stages]
+    st.run()
+    torch.cuda.synchronize()
+    assert st.error() == 0
+    for (_, _, ys, *_), f in zip(stages, first):
+        for t, ft in zip(ys, f):
+            assert torch.equal(t, ft)
+
+
 def test_stack_fp32_outputs_match_oracle():
     """fp32 outputs of an unchained layer against the fp64 oracle."""
     import torch
@@ -127,3 +177,10 @@ def test_stack_rejects_bad_stages():
     with pytest.raises(qw.QwError) as e:
         qw.Stack([([pw2], x2, [y])])
     assert e.value.status == qw.QW_ERR_UNSUPPORTED
+    with pytest.raises(ValueError):  # one merged weight per swiglu stage
+        qw.Stack([([pw, pw], x, [y, y], True)])
+    _, pw3, _ = _packed(48, 1024, 252, frac=0)  # N = 48: not two halves of whole tiles
+    y3 = torch.zeros(24, dtype=torch.float16, device="cuda")
+    with pytest.raises(qw.QwError) as e:
+        qw.Stack([([pw3], x, [y3], True)])
+    assert e.value.status == qw.QW_ERR_INVALID_ARG
