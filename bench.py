@@ -98,6 +98,9 @@ class Workload:
     def kernel_amount(self):  # per-launch algorithmic amount by kernel name
         raise NotImplementedError
 
+    def kernel_bytes(self):  # per-launch algorithmic bytes by kernel name
+        return self.kernel_amount() if self.unit == "GB/s" else {}
+
     def config(self):
         raise NotImplementedError
 
@@ -514,6 +517,10 @@ class Prefill70b(Workload):
     def kernel_amount(self):
         return {"qgemm_prefill": 2.0 * self.M * self.N * self.K}
 
+    def kernel_bytes(self):  # X, the packed weight and Y, each once
+        z = self.qw.qw_packed_sizes(self.fmt, self.N, self.K, 0)
+        return {"qgemm_prefill": self.M * self.K * 2 + z["codes"] + z["scales"] + self.M * self.N * 2}
+
     def step_amount(self):
         return 2.0 * self.M * self.N * self.K
 
@@ -865,11 +872,15 @@ def measure(wl, steps, warmup, traffic_json):
     value = wl.step_amount() / (ms_per_step * 1e-3) / scale
 
     amounts = wl.kernel_amount()
+    kbytes = wl.kernel_bytes()
     kstats = {}
     for nm, ds in per_kernel.items():
         avg = float(np.mean(ds))
         kstats[nm] = {"avg_us": round(avg * 1e3, 3), "launches": len(ds),
-                      "achieved": round(amounts[nm] / (avg * 1e-3) / scale, 2)}
+                      "achieved": round(amounts[nm] / (avg * 1e-3) / scale, 2),
+                      "amount": int(amounts[nm])}  # algorithmic bytes (flops) per launch
+        if nm in kbytes and kbytes[nm] != amounts[nm]:
+            kstats[nm]["bytes"] = int(kbytes[nm])  # algorithmic bytes of a flop-bound launch
     dominant = max(kstats, key=lambda k: kstats[k]["avg_us"] * kstats[k]["launches"])
     peak = BF16_PEAK_TFLOPS if wl.bound == "mfma" else HBM_PEAK_GBS
     ach = kstats[dominant]["achieved"]
