@@ -162,14 +162,18 @@ int qw_outlier_count(int K, double frac);
 qw_status qw_codebook_2bit(float *out);
 
 /* The 16 NF4 levels the library uses, ascending, as fp32, into host array
- * out[16]. Built on the host at first use from normal quantiles: 8 positive
+ * out[16] ("AirQuant" README, item 2 and "Fontes": NF4 as in QLoRA; the
+ * page prints no level, so the construction is this library's reading of
+ * QLoRA's). Built on the host at first use from normal quantiles: 8 positive
  * at probabilities evenly spaced from delta down to 1/2 (exclusive), 7
  * negative likewise, plus 0, divided by the largest;
  * delta = 1 - (1/32 + 1/30)/2. */
 qw_status qw_nf4_levels(float *out);
 
-/* Bytes of the device workspace the two selectors need for K channels
- * (K * 20; 0 when K <= 0). Host only. */
+/* Bytes of the device workspace the selectors of section 4 (OTF-LLM page:
+ * profile-guided outlier channels) and the INT4 permutation need for K
+ * channels (K * 20: fp64 scores, profile sums, int32 flags; 0 when K <= 0).
+ * Host only. */
 size_t qw_select_workspace_bytes(int K);
 
 /* Profile-guided outlier selection (section 4 of the OTF-LLM page).
@@ -203,7 +207,10 @@ qw_status qw_select_perm(const float *W, int N, int K, const float *X_prof, int 
                          size_t workspace_bytes, void *stream);
 
 /* Columns of X in permuted order: X_p[m][j] = X[m][perm[j]] (the order in
- * which the INT4 products take their activations).
+ * which the INT4 products take their activations: the OTF-LLM page's
+ * "Comparative Analysis" names a global static permutation of the v3.2
+ * format; reading it as a reordering of the channel space done once, the
+ * activations are gathered with it).
  *   X      device [M][K], elements of dtype (F16, BF16 or F32)
  *   perm   device int32 [K], a permutation of 0..K-1 (not checked; entries
  *          out of range read zero)
@@ -315,7 +322,8 @@ qw_status qgemv_2bit(const qw_weight *w, const void *x, int B, void *y,
                      qw_dtype y_dtype, void *stream);
 
 /* Device workspace bytes qgemv_2bit_ws needs for weight w at batch B (into
- * host *bytes): 0 when the call runs without one, else parts * B * N * 4
+ * host *bytes; the K split is this library's, the pages being silent on
+ * batched decode): 0 when the call runs without one, else parts * B * N * 4
  * for the fp32 partial rows of its K parts (parts <= 8). Host only; the
  * answer depends on the shape and on the current device. Errors as
  * qgemv_2bit's argument checks. */
@@ -375,7 +383,9 @@ qw_status qgemv_nf4(const qw_weight *w, const void *x, int B, void *y,
                     qw_dtype y_dtype, void *stream);
 
 /* Several 2-bit decode GEMVs that share one input x (for example the q, k
- * and v projections of one attention block), in one launch:
+ * and v projections of one attention block), in one launch (fewer launches
+ * per token for the streaming bound of the OTF-LLM page's section 1; the
+ * products are those of qgemv_2bit):
  *   y_i = qgemv_2bit(w_i, x) for i < count (count <= 4), bit for bit.
  * All w_i must have the same K; y_i have their own N_i. Same conventions as
  * qgemv_2bit (no workspace); ws and ys are host arrays of count entries. */
