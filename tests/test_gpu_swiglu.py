@@ -32,8 +32,10 @@ def _run(pw, x16, f32):
 
 
 # (I, K): one tile pair, several pairs with a ragged share per workgroup,
-# more pairs than workgroups, the 32B block's hidden size
-SHAPES = [(16, 512), (48, 1024), (272, 2048), (1040, 5120)]
+# an odd and an even workgroup count (the even one splits each CU's share of
+# pairs between two workgroups, unevenly here: 600 pairs, 512 workgroups),
+# the 32B block's hidden size
+SHAPES = [(16, 512), (48, 1024), (272, 2048), (9600, 512), (1040, 5120)]
 
 
 @pytest.mark.parametrize("I,K", SHAPES)
