@@ -112,6 +112,21 @@ def test_validation_before_device_work(L):
     # anchors declared without buffers
     va = qw.qw_weight(qw.QW_FMT_2BIT_G32, 16, 64, 3, 8, 0x1000, 0x1000, None, None, None)
     assert L.qgemv_2bit(ctypes.byref(va), p, 1, p, qw.QW_DT_F16, s) == qw.QW_ERR_INVALID_ARG
+    # merged gate/up GEMV: weight view, batch, dtype, N = 2I with I % 16 == 0,
+    # pointers; all refused before any device query
+    v32 = _view(qw.QW_FMT_2BIT_G32, 32, 64)
+    assert L.qgemv_2bit_swiglu(None, p, 1, p, qw.QW_DT_F16, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qgemv_2bit_swiglu(ctypes.byref(v32), p, 0, p, qw.QW_DT_F16, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qgemv_2bit_swiglu(ctypes.byref(v32), p, 9, p, qw.QW_DT_F16, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qgemv_2bit_swiglu(ctypes.byref(v32), p, 1, p, qw.QW_DT_BF16, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qgemv_2bit_swiglu(ctypes.byref(v32), None, 1, p, qw.QW_DT_F16, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qgemv_2bit_swiglu(ctypes.byref(v32), p, 1, None, qw.QW_DT_F16, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qgemv_2bit_swiglu(ctypes.byref(v), p, 1, p, qw.QW_DT_F16, s) == qw.QW_ERR_INVALID_ARG  # N = 16
+    v48 = _view(qw.QW_FMT_2BIT_G32, 48, 64)
+    assert L.qgemv_2bit_swiglu(ctypes.byref(v48), p, 1, p, qw.QW_DT_F16, s) == qw.QW_ERR_INVALID_ARG
+    assert L.qgemv_2bit_swiglu(ctypes.byref(v32), odd, 1, p, qw.QW_DT_F16, s) == qw.QW_ERR_ALIGNMENT
+    vn4 = _view(qw.QW_FMT_NF4_B64, 32, 64)
+    assert L.qgemv_2bit_swiglu(ctypes.byref(vn4), p, 1, p, qw.QW_DT_F16, s) == qw.QW_ERR_INVALID_ARG
     # prefill needs K % 64
     v96 = _view(qw.QW_FMT_2BIT_G32, 16, 96)
     assert L.qgemm_prefill(ctypes.byref(v96), p, 4, p, qw.QW_DT_F32, s) == qw.QW_ERR_UNSUPPORTED
