@@ -34,11 +34,14 @@
 //    lane that owns it.
 // Work: a wave computes 16 output rows; its K range is cut in super-chunks of
 // 512 (16 groups, 4 instructions per stream), streamed through a ring of P
-// register slots (two 16-byte code loads and two 8-byte S/Z loads per lane),
+// register slots (two 16-byte code loads and one 16-byte S/Z load per lane),
 // followed by anchor chunks of 96 anchors per row on the same ring.
 // A workgroup of 8 waves owns a contiguous range of 16-row tiles; each tile's
 // K range may be split over several waves, whose partial row sums meet in LDS
 // and are added in a fixed order.
+// The same body serves the merged gate/up product (pairs of gate and up tiles
+// per workgroup, silu(gate) * up in the epilogue), the K parts of wide
+// batches, and the persistent decode stack at the end of this file.
 #include <stdlib.h>
 
 #include <mutex>
@@ -60,12 +63,9 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kXItems = 12;  // 16-byte x loads per thread in the prologue
 constexpr int kIdxItems = 4; // anchor indices per thread in the prologue
 constexpr int kAnchorChunk = 96;
-#ifndef QW_GEMV_EARLY_SLOTS
-#define QW_GEMV_EARLY_SLOTS 2
-#endif
 // ring slots requested before the x preparation (the rest after it): more
 // start the weight stream earlier but delay the preparation behind them
-constexpr int kEarly = QW_GEMV_EARLY_SLOTS;
+constexpr int kEarly = 2;
 constexpr uint32_t kOob = 0x7FFFFFF0u;
 
 struct Mat {
