@@ -253,6 +253,49 @@ def test_gemv_2bit_matrix_core_and_vector_paths(N, K, n_anchor, B, tune):
     assert e_mc <= TOL_F32_GEMV and e_va <= TOL_F32_GEMV
 
 
+def test_gemv_2bit_largest_k_each_path(tune):
+    """The largest rows each kernel takes whole at batch 1: K = 40960 on the
+    matrix cores (its x limbs and 1433 anchor slots fill most of the LDS, the
+    anchors gathered from global x) and K = 32736 on the vector ALUs (the
+    prepared x takes 5 K bytes of the 160 KB); both against the oracle with
+    3.5% anchors. At K = 40960 batch 2 needs K parts: through a workspace it
+    runs, without one it is refused."""
+    import torch
+    for K, path in ((40960, 0), (32736, 1)):
+        W = inputs.weight(48, K, workload=85)
+        X = inputs.profile(32, K, workload=85)
+        idx = oracle.select_outliers(W, X, 0.035)
+        x = inputs.act_f16(2, K, workload=85)
+        pw = _packed_2bit(W, idx)
+        tune(qw.QW_TUNE_GEMV2_PATH, path)
+        y = _run_2bit(pw, x[:1], f32=True)
+        e = norm_err(y, _ref_2bit(W, x[:1], idx))
+        print(f"48x{K} anchors={len(idx)} path={path}: err {e:.3e}")
+        assert e <= TOL_F32_GEMV
+        if K == 40960:
+            ws = qw.gemv_workspace(pw, 2)
+            assert ws is not None
+            y2 = qw.qgemv_2bit_ws(pw, f16_dev(x), ws, out_dtype=torch.float32).cpu().numpy()
+            assert norm_err(y2, _ref_2bit(W, x, idx)) <= TOL_F32_GEMV
+            with pytest.raises(qw.QwError) as ex:
+                qw.qgemv_2bit(pw, f16_dev(x))
+            assert ex.value.status == qw.QW_ERR_UNSUPPORTED
+
+
+def test_gemv_2bit_half_the_channels_anchored():
+    """A degenerate anchor set: half of the channels (every second one,
+    including the first and the last group's edges) kept in fp16."""
+    K = 1024
+    W = inputs.weight(40, K, workload=86)
+    idx = np.arange(1, K, 2, dtype=np.int32)
+    idx[0] = 0
+    x = inputs.act_f16(3, K, workload=86)
+    pw = _packed_2bit(W, idx)
+    e = norm_err(_run_2bit(pw, x, f32=True), _ref_2bit(W, x, idx))
+    print(f"40x{K} with {len(idx)} anchors: err {e:.3e}")
+    assert e <= TOL_F32_GEMV
+
+
 @pytest.mark.parametrize("N,K,n_anchor,B", [(1024, 5120, 179, 1), (2048, 2048, 0, 1), (11008, 4096, 0, 1),
                                             (1000, 5120, 179, 3), (64, 3072, 40, 2)])
 def test_gemv_2bit_ring_depth_same_bits(N, K, n_anchor, B, tune):
