@@ -73,8 +73,8 @@ void build_nf4() {
 }  // namespace
 
 // Test hooks (qw_tuning.h), indexed by key; -1 = automatic.
-constexpr int kTuneKeys = 6;
-std::atomic<int> g_tune[kTuneKeys] = {{-1}, {-1}, {-1}, {-1}, {-1}, {-1}};
+constexpr int kTuneKeys = 7;
+std::atomic<int> g_tune[kTuneKeys] = {{-1}, {-1}, {-1}, {-1}, {-1}, {-1}, {-1}};
 
 int tune(qw_tune_key key) {
   const int k = (int)key;

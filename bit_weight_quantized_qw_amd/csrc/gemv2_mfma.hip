@@ -45,6 +45,7 @@
 #include <stdlib.h>
 
 #include <mutex>
+#include <type_traits>
 #include <vector>
 
 #include "qw_internal.h"
@@ -153,10 +154,11 @@ __device__ inline u32x4 ld4_coherent(__amdgpu_buffer_rsrc_t r, uint32_t v, uint3
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)v, (int)s, kCoherent);
 }
 
-__device__ inline v4f mfma_x_codes(v8i a_fp8, v8i b_fp4) {
-  const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-  // A format 0 = e4m3, B format 4 = e2m1; scales 0x7f = 2^0
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_fp8, b_fp4, z, 0, 4, 0, 0x7f, 0, 0x7f);
+// B scaled by 2^(scale_b - 127) (e8m0), added to c
+__device__ inline v4f mfma_x_codes(v8i a_fp8, v8i b_fp4, v4f c = v4f{0.0f, 0.0f, 0.0f, 0.0f},
+                                   int scale_b = 0x7f) {
+  // A format 0 = e4m3, B format 4 = e2m1; A scale 0x7f = 2^0
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a_fp8, b_fp4, c, 0, 4, 0, 0x7f, 0, scale_b);
 }
 
 __device__ inline float h2f(uint32_t bits16) {
@@ -235,6 +237,13 @@ struct Stream {
 struct Slot {
   u32x4 c0, c1, c2;
 };
+// INT4 (v3.2 format): code step: the 32 codes of four groups (four 16-byte
+// loads) and their four fp16 scales (one 8-byte load); anchor step: three
+// pieces of 8 anchor weights in c0..c2 (c3 and sz then read zeros).
+struct Slot4 {
+  u32x4 c0, c1, c2, c3;
+  u32x2 sz;
+};
 
 // Select among four values that are all read (so the reads are not
 // conditional: no chain of dependent scalar loads behind branches).
@@ -255,8 +264,22 @@ __device__ inline T sel4(int i, T v0, T v1, T v2, T v3) {
 // (a.swiglu == 1, a single matrix): the workgroup's items are tile pairs, the
 // gate tile p and the up tile H + p (H = I / 16), so both factors of each of
 // its outputs meet in its own LDS.
-template <int B, int P, bool MULTI, bool XC = false, bool XR = true, int NT = kThreads, bool SW = false>
+// I4: the v3.2 INT4 format ("On-The-Fly Weight Synthesizer (OTF-LLM Engine
+// v4.0)", "Comparative Analysis: INT4 (v3.2) vs INT2 Non-Uniform (v4.0)"):
+// codes u = q + 8 two per byte in element order, an fp16 scale s per group
+// of 32, no anchor mask (anchor columns hold the zero level), anchors at
+// the first n_out positions of x (x given in permuted order). A nibble
+// u3 u2 u1 u0 masked to its low two bits is the e2m1 value (2 u1 + u0) / 2,
+// its high two bits shifted down the value (2 u3 + u2) / 2, so
+// u / 2 = P_lo + 4 P_hi: two fp4 products accumulated in one register, the
+// second with the operand scale 2^2 of the scaled matrix-core instruction;
+// per group sum x q = 2 (P_lo + 4 P_hi) - 8 X_g. x limbs are in element
+// order.
+template <int B, int P, bool MULTI, bool XC = false, bool XR = true, int NT = kThreads, bool SW = false,
+          bool I4 = false>
 __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds) {
+  static_assert(!I4 || (!MULTI && !SW && !XC), "INT4 runs single-matrix launches");
+  using SlotT = typename std::conditional<I4, Slot4, Slot>::type;
   constexpr int NW = NT / 64;
   // prologue items per thread: the same totals as at kThreads threads
   constexpr int XI = kXItems * kThreads / NT, IX = kIdxItems * kThreads / NT;
@@ -345,20 +368,21 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
   Stream st{n_units, W, L, NA, NW};
 
   // ---- per-lane load offsets ----
-  const uint32_t rb_c = (uint32_t)ldk / 4;         // code bytes per row
-  const uint32_t rb_s = (uint32_t)ldk / 8;         // S/Z bytes per row
+  const uint32_t rb_c = (uint32_t)ldk / (I4 ? 2 : 4);   // code bytes per row
+  const uint32_t rb_s = (uint32_t)ldk / (I4 ? 16 : 8);  // scale (S/Z) bytes per row
   const uint32_t rb_a = (uint32_t)ld_a * 2;        // anchor bytes per row
   const uint32_t lim_a = (uint32_t)M.n_out_pad * 2; // this part's anchor bytes per row
   // sizes from the part's first channel (anchor) to the end of the matrix
-  const uint32_t n_codes = (uint32_t)((size_t)M.N * rb_c - (uint32_t)kbase / 4);
-  const uint32_t n_sz = (uint32_t)((size_t)M.N * rb_s - (uint32_t)kbase / 8);
+  const uint32_t n_codes = (uint32_t)((size_t)M.N * rb_c - (uint32_t)kbase / (I4 ? 2 : 4));
+  const uint32_t n_sz = (uint32_t)((size_t)M.N * rb_s - (uint32_t)kbase / (I4 ? 16 : 8));
   const uint32_t n_wo = (uint32_t)((size_t)M.N * rb_a - (uint32_t)abase * 2);
 
   // ring slot: code step: lane (row j, slot g) takes groups 16 sc + 4g ..
   // +3 of its row: codes bytes [32g, 32g+32) of the super-chunk's 128 and
-  // their four S/Z words. Anchor step: three pieces of 8 anchor weights. One
+  // their four S/Z words (INT4: bytes [64g, 64g+64) of 256 and four fp16
+  // scales). Anchor step: three pieces of 8 anchor weights. One
   // branch-free issue path: descriptor and offsets are picked per step kind.
-  auto issue = [&](Slot &dst, const Cursor &c) __attribute__((always_inline)) {
+  auto issue = [&](SlotT &dst, const Cursor &c) __attribute__((always_inline)) {
     const bool live = c.unit < n_units;
     const int lt = live ? c.tile : 0;
     const int tile = SW ? (lt < np ? t0 + lt : H + t0 + (lt - np)) : t0 + lt;
@@ -372,11 +396,33 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
                           !live ? 0u : (code ? n_codes : n_wo));
     const auto r2 = rsrc(code ? (const void *)M.sz : (const void *)M.wo,
                          !live ? 0u : (code ? n_sz : n_wo));
-    const uint32_t s01 = !live ? 0u : (code ? (uint32_t)tile * 16 * rb_c + (uint32_t)sc * 128
+    const uint32_t s01 = !live ? 0u : (code ? (uint32_t)tile * 16 * rb_c + (uint32_t)sc * (I4 ? 256 : 128)
                                             : (uint32_t)tile * 16 * rb_a);
-    const uint32_t s2 = !live ? 0u : (code ? (uint32_t)tile * 16 * rb_s + (uint32_t)sc * 64
+    const uint32_t s2 = !live ? 0u : (code ? (uint32_t)tile * 16 * rb_s + (uint32_t)sc * (I4 ? 32 : 64)
                                            : (uint32_t)tile * 16 * rb_a);
     const uint32_t pa = (uint32_t)an * (kAnchorChunk * 2) + 16u * g;  // anchor piece 0
+    if constexpr (I4) {
+      // code step: four 16-byte code loads and one 8-byte scale load; anchor
+      // step: the three anchor pieces (all from r01), the rest read zeros
+      uint32_t v[4], vs;
+      if (code) {  // uniform
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = row_ok ? (uint32_t)j * rb_c + 64u * g + 16u * t : kOob;
+        vs = row_ok ? (uint32_t)j * rb_s + 8u * g : kOob;
+      } else {
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+          v[t] = row_ok && pa + 64u * t < lim_a ? (uint32_t)j * rb_a + pa + 64u * t : kOob;
+        v[3] = kOob;
+        vs = kOob;
+      }
+      dst.c0 = ld4(r01, v[0], s01);
+      dst.c1 = ld4(r01, v[1], s01);
+      dst.c2 = ld4(r01, v[2], s01);
+      dst.c3 = ld4(r01, v[3], s01);
+      dst.sz = ld2(r2, vs, s2);
+      return;
+    }
     uint32_t v0, v1, v2;
     if (code) {  // uniform
       v0 = row_ok ? (uint32_t)j * rb_c + 32u * g : kOob;
@@ -389,7 +435,7 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
     }
     dst.c0 = ld4(r01, v0, s01);
     dst.c1 = ld4(r01, v1, s01);
-    dst.c2 = ld4(r2, v2, s2);
+    if constexpr (!I4) dst.c2 = ld4(r2, v2, s2);
   };
 
   // ---- prologue loads: x (16 bytes per item), anchor mask, anchor indices ----
@@ -399,7 +445,7 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
   const auto r_idx = rsrc(M.idx, (uint32_t)M.n_out * 4);
   u32x4 xv[XI];
   uint32_t mk[XI];
-  const bool has_mask = M.mask != nullptr;
+  const bool has_mask = !I4 && M.mask != nullptr;
 #pragma unroll
   for (int q = 0; q < XI; ++q) {
     xv[q] = u32x4{0, 0, 0, 0};
@@ -423,12 +469,13 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
     aidx[q] = 0;
     if (q * NT < M.n_out) {  // uniform
       const int o = q * NT + tid;
-      aidx[q] = ld1(r_idx, o < M.n_out ? (uint32_t)o * 4 : kOob, 0);
+      // INT4: the anchors are the first n_out positions of x
+      aidx[q] = I4 ? (uint32_t)o : ld1(r_idx, o < M.n_out ? (uint32_t)o * 4 : kOob, 0);
     }
   }
   // ---- weight prefetch: the first P steps (every ring load is
   //      unconditional, so the waits below count exactly) ----
-  Slot ring[P];
+  SlotT ring[P];
   Cursor cl = st.start(wave);
   __builtin_amdgcn_sched_barrier(0);
   constexpr int E = kEarly < P ? kEarly : P;
@@ -453,7 +500,15 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
 #pragma unroll
       for (int t = 1; t < B; ++t) b += bg >= t * G;
       const int gr = bg - b * G;
-        const uint32_t om = (mk[q] >> (qt * 8)) & 0xFFu;
+        // channels read as zero: the anchors (their code is the zero level
+        // for INT4, so zeroing them there changes no product)
+        uint32_t om;
+        if constexpr (I4) {
+          const int na = M.n_out - (gr * 32 + qt * 8);  // INT4 launches are unsplit
+          om = na >= 8 ? 0xFFu : (na <= 0 ? 0u : (1u << na) - 1u);
+        } else {
+          om = (mk[q] >> (qt * 8)) & 0xFFu;
+        }
         uint32_t d[4] = {xv[q][0], xv[q][1], xv[q][2], xv[q][3]};
         if (ok && XR) {
           uint32_t *raw = reinterpret_cast<uint32_t *>(xraw + (size_t)b * KX + gr * 32 + qt * 8);
@@ -479,6 +534,27 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
         float r[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) r[i] = __builtin_ldexpf(xf[i], sh);
+        if constexpr (I4) {
+          // element order: element 8qt+i at byte 8(qt&1)+i of half qt/2
+          uint8_t *hb = limbs + ((size_t)(b * G + gr) * 3) * 32 + (qt >> 1) * 16 + 8 * (qt & 1);
+#pragma unroll
+          for (int lb = 0; lb < 3; ++lb) {
+            const uint32_t w0 = to_fp8x4(r[0], r[1], r[2], r[3]);
+            const uint32_t w1 = to_fp8x4(r[4], r[5], r[6], r[7]);
+            if (ok) *reinterpret_cast<u32x2 *>(hb + lb * 32) = u32x2{w0, w1};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              r[i] -= fp8_at(w0, i);
+              r[4 + i] -= fp8_at(w1, i);
+            }
+          }
+          if (ok && qt == 0) {
+            // sum x q = 2 (P_lo + 4 P_hi) - 8 X_g, P in units of 2^-sh
+            const float inv = __builtin_ldexpf(1.0f, -sh);
+            coef[b * G + gr] = make_float4(2.0f * inv, 0.0f, -8.0f * xs, xs);
+          }
+          continue;
+        }
         // element 8qt+i sits in half qt/2 at byte (i even) 4(qt&1)+i/2 or
         // (i odd) 8+4(qt&1)+i/2
         uint8_t *hb = limbs + ((size_t)(b * G + gr) * 3) * 32 + (qt >> 1) * 16 + 4 * (qt & 1);
@@ -566,9 +642,45 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
     }
   };
 
-  auto compute = [&](const Slot &src, const Cursor &c) __attribute__((always_inline)) {
+  auto compute = [&](const SlotT &src, const Cursor &c) __attribute__((always_inline)) {
     const int split = c.split;
-    if (c.step < L) {
+    if constexpr (I4) {
+      if (c.step < L) {
+        const int sc = split * L + c.step;
+        // chunk ch: this lane's group 16 sc + 4g + ch (code words c_ch), its
+        // nibbles split into the three e2m1 operands; chunks outermost, so
+        // only one chunk's operands are live
+        const uint8_t *p_lo = a_ok && !a_hi ? limbs + (size_t)(16 * sc) * 96 + a_lane : zero;
+        const uint8_t *p_hi = a_ok && a_hi ? limbs + (size_t)(16 * sc) * 96 + a_lane : zero;
+        const int st_lo = a_ok && !a_hi ? 96 : 0, st_hi = a_ok && a_hi ? 96 : 0;
+        const int bst_lo = a_ok && !a_hi ? G * 96 : 0, bst_hi = a_ok && a_hi ? G * 96 : 0;
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) {
+          const u32x4 cw = ch == 0 ? src.c0 : (ch == 1 ? src.c1 : (ch == 2 ? src.c2 : src.c3));
+          const uint32_t w0 = cw[0], w1 = cw[1], w2 = cw[2], w3 = cw[3];
+          const v8i blo = {(int)(w0 & 0x33333333u), (int)(w1 & 0x33333333u), (int)(w2 & 0x33333333u),
+                           (int)(w3 & 0x33333333u), 0, 0, 0, 0};
+          const v8i bhi = {(int)((w0 >> 2) & 0x33333333u), (int)((w1 >> 2) & 0x33333333u),
+                           (int)((w2 >> 2) & 0x33333333u), (int)((w3 >> 2) & 0x33333333u), 0, 0, 0, 0};
+          const uint32_t sw = src.sz[ch >> 1];
+          const float S = h2f((ch & 1) ? (sw >> 16) : (sw & 0xFFFFu));
+#pragma unroll
+          for (int b = 0; b < B; ++b) {
+            const u32x4 lo = *reinterpret_cast<const u32x4 *>(p_lo + b * bst_lo + ch * st_lo);
+            const u32x4 hi = *reinterpret_cast<const u32x4 *>(p_hi + b * bst_hi + ch * st_hi);
+            const v8i A = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                           (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+            const float4 cf = coef[b * G + 16 * sc + ch + 4 * g];
+            v4f d = mfma_x_codes(A, blo);
+            d = mfma_x_codes(A, bhi, d, 0x81);  // 2^2
+            const float pu = (d[0] + d[1]) + d[2];
+            acc[b] = __builtin_fmaf(S, __builtin_fmaf(pu, cf.x, cf.z), acc[b]);
+          }
+        }
+        return;
+      }
+    }
+    if (!I4 && c.step < L) {
       const int sc = split * L + c.step;
       // chunk ch covers groups 16 sc + ch + 4 s of slots s = 0..3; this
       // lane's codes and S/Z are those of slot g
@@ -624,18 +736,21 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
       }
     } else {
       const int an = split + W * (c.step - L);
-      const u32x4 pc[3] = {src.c0, src.c1, src.c2};
-#pragma unroll
-      for (int i = 0; i < 3; ++i) {
+      // pieces taken field by field (a copy of part of the slot into an
+      // array keeps the whole ring in private memory)
+      auto piece = [&](const u32x4 pc, int i) __attribute__((always_inline)) {
         const int o = an * kAnchorChunk + 8 * (g + 4 * i);
         // o + 8 <= xo_len always (xo_len is a multiple of 96)
 #pragma unroll
         for (int b = 0; b < B; ++b) {
           const u32x4 xv4 = *reinterpret_cast<const u32x4 *>(xo + b * a.xo_len + o);
 #pragma unroll
-          for (int p = 0; p < 4; ++p) acc[b] = dot2(xv4[p], pc[i][p], acc[b]);
+          for (int p = 0; p < 4; ++p) acc[b] = dot2(xv4[p], pc[p], acc[b]);
         }
-      }
+      };
+      piece(src.c0, 0);
+      piece(src.c1, 1);
+      piece(src.c2, 2);
     }
   };
 
@@ -729,6 +844,13 @@ template <int B, int P, bool MULTI, bool XR = true, bool SW = false>
 __global__ __launch_bounds__(kThreads) void kernel(Args a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   body<B, P, MULTI, false, XR, kThreads, SW>(a, (int)blockIdx.x, lds);
+}
+
+// The v3.2 INT4 format on the same body (one matrix, 3-slot ring, unsplit).
+template <int B, bool XR>
+__global__ __launch_bounds__(kThreads) void kernel_int4(Args a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  body<B, 3, false, false, XR, kThreads, false, true>(a, (int)blockIdx.x, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -852,6 +974,29 @@ qw_status launch_bp(const Args &a, int grid, size_t lds, hipStream_t s) {
                     : launch_bpmx<B, P, false, false, true>(a, grid, lds, s);
   }
   return a.count > 1 ? launch_bpm<B, P, true>(a, grid, lds, s) : launch_bpm<B, P, false>(a, grid, lds, s);
+}
+
+template <int B>
+qw_status launch_int4_b(const Args &a, int grid, size_t lds, hipStream_t s) {
+  auto fn = a.xraw ? kernel_int4<B, true> : kernel_int4<B, false>;
+  if (lds > 64 * 1024)
+    QW_HIP_TRY(hipFuncSetAttribute(reinterpret_cast<const void *>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)lds));
+  QW_HIP_TRY(launch(fn, grid, kThreads, lds, s, a));
+  return QW_OK;
+}
+
+qw_status launch_int4_sel(const Args &a, int B, int grid, size_t lds, hipStream_t s) {
+  switch (B) {
+    case 1: return launch_int4_b<1>(a, grid, lds, s);
+    case 2: return launch_int4_b<2>(a, grid, lds, s);
+    case 3: return launch_int4_b<3>(a, grid, lds, s);
+    case 4: return launch_int4_b<4>(a, grid, lds, s);
+    case 5: return launch_int4_b<5>(a, grid, lds, s);
+    case 6: return launch_int4_b<6>(a, grid, lds, s);
+    case 7: return launch_int4_b<7>(a, grid, lds, s);
+    default: return launch_int4_b<8>(a, grid, lds, s);
+  }
 }
 
 // Ring depth: 3 slots, or the deep ring (6 slots up to batch 2, 4 beyond).
@@ -1233,6 +1378,40 @@ qw_status launch_swiglu(const qw_weight &w, const uint16_t *x, int B, void *y, b
     as.m[0].y = reinterpret_cast<char *>(y) + (size_t)b0 * (w.N / 2) * esz;
     const size_t lds = lds_layout(bs, K, a.xo_len, a.units_max, a.xraw).total;
     QW_TRY(launch_b(as, bs, false, grid, lds, s));
+    b0 += bs;
+  }
+  return QW_OK;
+}
+
+// The INT4 (v3.2) decode GEMV on the matrix cores (y: [B][N]), unsplit, in
+// balanced batch slices as above. Returns QW_ERR_UNSUPPORTED (nothing
+// enqueued) when the shape does not fit (K not a multiple of 512, more
+// anchors than the gather takes, no slice of two or more rows fits); the
+// caller then uses the vector-ALU kernel. The caller has validated the
+// view and checked N * K / 2 < 2^31.
+qw_status launch_int4(const qw_weight &w, const uint16_t *x, int B, void *y, bool f32, int cus,
+                      hipStream_t s) {
+  if (B < 1 || B > 8) return QW_ERR_UNSUPPORTED;
+  const int K = w.K;
+  Args a;
+  int grid = 0;
+  void *ys[1] = {y};
+  QW_TRY(plan(&w, 1, x, ys, f32, cus, a, grid));
+  a.m[0].mask = nullptr;  // anchors: the first n_out positions
+  a.m[0].idx = nullptr;
+  int xr = 1, bmax = 0;
+  const int n_slices = unsplit_slices(a, B, &xr, &bmax);
+  if (n_slices == 0) return QW_ERR_UNSUPPORTED;
+  a.xraw = xr;
+  const size_t esz = f32 ? 4 : 2;
+  int b0 = 0;
+  for (int sl = 0; sl < n_slices; ++sl) {
+    const int bs = (B - b0 + (n_slices - sl) - 1) / (n_slices - sl);
+    Args as = a;
+    as.x = x + (size_t)b0 * K;
+    as.m[0].y = reinterpret_cast<char *>(y) + (size_t)b0 * w.N * esz;
+    const size_t lds = lds_layout(bs, K, a.xo_len, a.units_max, a.xraw).total;
+    QW_TRY(launch_int4_sel(as, bs, grid, lds, s));
     b0 += bs;
   }
   return QW_OK;

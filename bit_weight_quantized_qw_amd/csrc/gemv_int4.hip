@@ -28,6 +28,11 @@
 #include "qw_internal.h"
 
 namespace qw {
+namespace gemv2m {
+qw_status launch_int4(const qw_weight &w, const uint16_t *x, int B, void *y, bool f32, int cus,
+                      hipStream_t s);
+}  // namespace gemv2m
+
 namespace {
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -333,9 +338,14 @@ extern "C" qw_status qgemv_int4(const qw_weight *w, const void *x, int B, void *
   if (st != QW_OK) return st;
   const int K = w->K, N = w->N;
   if ((size_t)N * (K / 2) >= (1ull << 31)) return QW_ERR_UNSUPPORTED;
+  const bool f32 = y_dtype == QW_DT_F32;
+  // the matrix-core kernel where it takes the shape, else this file's kernel
+  if (tune(QW_TUNE_INT4_PATH) != 1) {
+    st = gemv2m::launch_int4(*w, reinterpret_cast<const uint16_t *>(x), B, y, f32, cus, as_stream(stream));
+    if (st != QW_ERR_UNSUPPORTED) return st;
+  }
   const int NG = K / 32;
   const int n_pad = w->n_out > 0 ? w->n_out_pad : 0;
-  const bool f32 = y_dtype == QW_DT_F32;
   const size_t esz = f32 ? 4 : 2;
   const int rpg = (int)max(1L, ((long)N + cus - 1) / cus);  // one workgroup per CU
   const int grid = (N + rpg - 1) / rpg;

@@ -38,7 +38,7 @@ EXPORTS = [
 
 # test hooks (include/qw_tuning.h)
 QW_TUNE_GEMV2_PATH, QW_TUNE_GEMV2_SPLIT, QW_TUNE_GEMV2_DEEP_RING = 1, 2, 3
-QW_TUNE_NF4_DEEP_RING, QW_TUNE_PREFILL_WIDE_TILES = 4, 5
+QW_TUNE_NF4_DEEP_RING, QW_TUNE_PREFILL_WIDE_TILES, QW_TUNE_INT4_PATH = 4, 5, 6
 QW_TUNE_AUTO = -1
 
 

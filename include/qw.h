@@ -369,9 +369,12 @@ qw_status qgemv_2bit_static(const qw_weight *w, const void *x, int B, void *y,
  * with x_p the activations in permuted channel order (qw_permute_cols).
  *   x_p device fp16 [B][K], 1 <= B <= 8
  *   y   device [B][N], fp16 (nearest-even) or fp32
- * fp32 accumulation; no workspace. Batches whose x does not fit one
- * workgroup whole run as row groups. Errors: INVALID_ARG, ALIGNMENT,
- * UNSUPPORTED, HIP. */
+ * fp32 accumulation; no workspace. Where K is a multiple of 512 the
+ * products run on the matrix cores (the 2-bit GEMV's scheme: the code bits
+ * as fp4 operands against exact fp8 limbs of x), batches in slices whose x
+ * fits one workgroup; other shapes on the vector ALUs, in row groups. The
+ * results of the two kernels agree within the fp32 bound, not bit for bit.
+ * Errors: INVALID_ARG, ALIGNMENT, UNSUPPORTED, HIP. */
 qw_status qgemv_int4(const qw_weight *w, const void *x_p, int B, void *y,
                      qw_dtype y_dtype, void *stream);
 

@@ -37,7 +37,10 @@ typedef enum {
   QW_TUNE_NF4_DEEP_RING = 4,
   /* Prefill without anchors: -1 automatic, n >= 0 the number of 256-wide
    * column tiles (the rest runs as 128-wide tiles). */
-  QW_TUNE_PREFILL_WIDE_TILES = 5
+  QW_TUNE_PREFILL_WIDE_TILES = 5,
+  /* INT4 GEMV kernel: -1 / 0 the matrix-core kernel wherever it takes the
+   * shape, 1 the vector-ALU kernel. */
+  QW_TUNE_INT4_PATH = 6
 } qw_tune_key;
 
 #define QW_TUNE_AUTO (-1)

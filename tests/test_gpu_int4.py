@@ -102,6 +102,52 @@ def test_gemv_small(N, K, n_out, B):
     np.testing.assert_array_equal(y16.astype(np.float16), y32.astype(np.float16))
 
 
+# (N, K, n_out, B): batches the matrix-core kernel takes in one pass (with
+# and without the raw x copy) and in slices (8 rows of K = 8192 as 3 + 3 + 2)
+@pytest.mark.parametrize("N,K,n_out,B", [(200, 3072, 30, 1), (200, 3072, 30, 8), (300, 8192, 81, 3),
+                                         (300, 8192, 81, 8), (50, 16384, 163, 1), (64, 5120, 51, 8)])
+def test_gemv_both_kernels(N, K, n_out, B, tune):
+    """Shapes the matrix-core kernel takes, run on it and, forced, on the
+    vector-ALU kernel: both within the fp32 bound of the oracle. Their low
+    bits differ (the two sum in different orders), which shows that the two
+    calls ran different kernels."""
+    W = inputs.weight(N, K, workload=117)
+    perm = np.random.default_rng(N * K).permutation(K).astype(np.int32)
+    r = oracle.quantize_int4(W, perm, n_out)
+    pw = _pack(W, perm, n_out)
+    x_p = oracle.permute_cols(inputs.act_f16(B, K, workload=117), perm)
+    ref = oracle.gemv_int4_ref(x_p, r["q"], r["s"], r["W_O"])
+    ys = []
+    for path in (0, 1):
+        tune(qw.QW_TUNE_INT4_PATH, path)
+        y = _gemv(pw, x_p)
+        e = norm_err(y, ref)
+        print(f"int4 {N}x{K} anchors={n_out} B={B} path={path}: err {e:.3e}")
+        assert e <= TOL_F32_GEMV
+        ys.append(y)
+    assert not np.array_equal(ys[0], ys[1])
+
+
+def test_gemv_largest_k(tune):
+    """The largest rows the matrix-core kernel takes whole at batch 1:
+    K = 28672 with the raw x copy in LDS and K = 40960 without it (anchors
+    gathered from global x), 1% anchors (287 and 409: several gather
+    chunks); batch 2 at K = 40960 does not fit it and runs on the
+    vector-ALU kernel. All against the oracle."""
+    for K in (28672, 40960):
+        N = 48
+        W = inputs.weight(N, K, workload=116)
+        perm = np.random.default_rng(K).permutation(K).astype(np.int32)
+        n_out = oracle.outlier_count(K, 0.01)
+        r = oracle.quantize_int4(W, perm, n_out)
+        pw = _pack(W, perm, n_out)
+        x_p = oracle.permute_cols(inputs.act_f16(2, K, workload=116), perm)
+        for B in (1, 2):
+            e = norm_err(_gemv(pw, x_p[:B]), oracle.gemv_int4_ref(x_p[:B], r["q"], r["s"], r["W_O"]))
+            print(f"int4 {N}x{K} anchors={n_out} B={B}: err {e:.3e}")
+            assert e <= TOL_F32_GEMV
+
+
 def test_gemv_one_hot_and_zero_inputs():
     N, K, n_out = 40, 2048, 20
     W = inputs.weight(N, K, workload=115)

@@ -182,7 +182,7 @@ def test_tuning_hooks_are_host_only(L):
     assert L.qw_tune_set(qw.QW_TUNE_GEMV2_PATH, -2) == qw.QW_ERR_INVALID_ARG
     assert qw.qw_tune_get(99) == qw.QW_TUNE_AUTO
     for key in (qw.QW_TUNE_GEMV2_PATH, qw.QW_TUNE_GEMV2_SPLIT, qw.QW_TUNE_GEMV2_DEEP_RING,
-                qw.QW_TUNE_NF4_DEEP_RING, qw.QW_TUNE_PREFILL_WIDE_TILES):
+                qw.QW_TUNE_NF4_DEEP_RING, qw.QW_TUNE_PREFILL_WIDE_TILES, qw.QW_TUNE_INT4_PATH):
         assert qw.qw_tune_get(key) == qw.QW_TUNE_AUTO
         with qw.tuned(key, 3):
             assert qw.qw_tune_get(key) == 3
