@@ -42,7 +42,7 @@ _C = "bit_weight_quantized_qw_amd/csrc/"
 _MC = [_C + "gemv2_mfma.hip", _C + "gemv2.hip", _C + "qw_internal.h"]
 _VALU = [_C + "gemv2_kernel.h", _C + "gemv2_b1.hip", _C + "gemv2.hip", _C + "qw_internal.h"]
 _NF4 = [_C + "gemv_nf4.hip", _C + "qw_internal.h"]
-_INT4 = [_C + "gemv_int4.hip", _C + "qw_internal.h"]
+_INT4 = [_C + "gemv2_mfma.hip", _C + "gemv_int4.hip", _C + "qw_internal.h"]
 _PF = [_C + "prefill.hip", _C + "qw_internal.h"]
 
 # workload -> bench kernel -> (dispatches of one call: [(name substring, grid
@@ -61,8 +61,9 @@ TRAFFIC = {
                         "o": ([("gemv2m::kernel", 131072)], 1, _MC),
                         "gateup": ([("gemv2m::kernel", 262144)], 1, _MC),
                         "down": ([("gemv2::kernel", None)], 1, _VALU)},
-    "decode14b_int4_b1": {"qgemv_int4": ([("gemv_int4_kernel", None)], 1, _INT4)},
-    "decode14b_int4_b8": {"qgemv_int4": ([("gemv_int4_kernel", None)], 1, _INT4)},
+    # the matrix-core INT4 kernel (K a multiple of 512)
+    "decode14b_int4_b1": {"qgemv_int4": ([("gemv2m::kernel_int4", None)], 1, _INT4)},
+    "decode14b_int4_b8": {"qgemv_int4": ([("gemv2m::kernel_int4", None)], 1, _INT4)},
     # 256-wide column tiles, then 128-wide ones for the last columns
     "prefill70b_2bit": {"qgemm_prefill": ([("prefill_w_kernel", None)], 2, _PF)},
     "prefill70b_nf4": {"qgemm_prefill": ([("prefill_w_kernel", None)], 2, _PF)},
