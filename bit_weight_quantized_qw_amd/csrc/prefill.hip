@@ -420,7 +420,9 @@ __global__ __launch_bounds__(256 * WM) void prefill_w_kernel(PrefillArgs a) {
   // of entry v at byte 256 v + 8 r, in bank pair r. Lane l reads replica
   // l % 16, so the table reads of 16 lanes never share a bank whatever the
   // codes (one 256-entry copy would collide about 3.5 ways per access).
-  __shared__ __attribute__((aligned(16))) char pair_tab[FMT != QW_FMT_2BIT_G32 ? 256 * 256 : 16];
+  // (NF4 only: 2-bit and INT4 fragments are built from registers alone)
+  constexpr bool kTab = FMT == QW_FMT_NF4_B64;
+  __shared__ __attribute__((aligned(16))) char pair_tab[kTab ? 256 * 256 : 16];
   const uint32_t lane_rep = 8u * (uint32_t)(threadIdx.x & 15);
 
   const int tid = threadIdx.x;
@@ -434,7 +436,7 @@ __global__ __launch_bounds__(256 * WM) void prefill_w_kernel(PrefillArgs a) {
   const int KT = K / BK;
   const int hk = lane >> 5;  // which 8 of each 16-wide k slice this lane holds
 
-  if (FMT != QW_FMT_2BIT_G32) {
+  if (kTab) {
     // 16-byte chunk c holds two replicas of entry c / 8
     for (int c = tid; c < 256 * 8; c += NTW) {
       const int v = c >> 3;
@@ -532,10 +534,25 @@ __global__ __launch_bounds__(256 * WM) void prefill_w_kernel(PrefillArgs a) {
     if (FMT == QW_FMT_2BIT_G32) {
       const int g = kk >> 1;
       dequant8_2bit(w[j][kk], hk, T[j][g][0], T[j][g][1], o);
+    } else if (FMT == QW_FMT_INT4_G32) {
+      // the fp16 scale s of group kk / 2; elements kk*16 + hk*8 .. +7 are
+      // the nibbles of code word 2kk + hk, element 2q in the low nibble of
+      // byte q. Each nibble u becomes a float exactly (byte to float), and
+      // u s - 8 s = (u - 8) s exactly (both products fit fp32), so the fma
+      // gives fl32(s q) before the one rounding to bf16.
+      const float s = f16_bits_to_f32((uint16_t)(w[j][8] >> (16 * (kk >> 1))));
+      const float ns8 = -8.0f * s;
+      // the word picked with a byte permute (a select here becomes an
+      // indexed read that moves the W registers to private memory)
+      const uint32_t c = __builtin_amdgcn_perm(w[j][2 * kk + 1], w[j][2 * kk], hk ? 0x07060504u : 0x03020100u);
+      const uint32_t lo = c & 0x0F0F0F0Fu, hi = (c >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = pack_bf16x2(__builtin_fmaf((float)((lo >> (8 * q)) & 0xFFu), s, ns8),
+                           __builtin_fmaf((float)((hi >> (8 * q)) & 0xFFu), s, ns8));
     } else {
-      // NF4: one fp32 absmax per 64; INT4: the fp16 scale of group kk / 2
-      const float am = FMT == QW_FMT_NF4_B64 ? __builtin_bit_cast(float, w[j][8])
-                                            : f16_bits_to_f32((uint16_t)(w[j][8] >> (16 * (kk >> 1))));
+      // NF4: one fp32 absmax per 64
+      const float am = __builtin_bit_cast(float, w[j][8]);
       // elements kk*16 + hk*8 .. +7 = bytes 4*(2kk+hk) .. +3 of the 32 code bytes
       const uint32_t c = hk ? w[j][2 * kk + 1] : w[j][2 * kk];
 #pragma unroll
@@ -569,12 +586,12 @@ __global__ __launch_bounds__(256 * WM) void prefill_w_kernel(PrefillArgs a) {
         }
     }
   };
-  // 2-bit: the tables and the first slice's B fragments of a step depend on
-  // the lane's own W registers only, so they are built during the previous
-  // step's last slice: after the step barrier only the A reads remain
-  // before the first products (measured 3.6% faster; the 4-bit formats,
-  // whose fragments read the LDS pair table, keep building them at the
-  // step start: 30% slower otherwise).
+  // 2-bit and INT4: the first slice's B fragments of a step (and the 2-bit
+  // tables) depend on the lane's own W registers only, so they are built
+  // during the previous step's last slice: after the step barrier only the
+  // A reads remain before the first products (measured 3.6% faster for
+  // 2-bit; NF4, whose fragments read the LDS pair table, keeps building
+  // them at the step start: 30% slower otherwise).
   uint32_t T[NJ][2][2];
   bf16x8 fb0[NJ];
 
@@ -587,7 +604,7 @@ __global__ __launch_bounds__(256 * WM) void prefill_w_kernel(PrefillArgs a) {
     bf16x8 fa[2][IM], fb[2][NJ];
     read_a(buf, 0, fa[0]);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) fb[0][j] = FMT == QW_FMT_2BIT_G32 ? fb0[j] : make_b(wr[PAR], j, 0, T);
+    for (int j = 0; j < NJ; ++j) fb[0][j] = !kTab ? fb0[j] : make_b(wr[PAR], j, 0, T);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
@@ -595,7 +612,7 @@ __global__ __launch_bounds__(256 * WM) void prefill_w_kernel(PrefillArgs a) {
         read_a(buf, kk + 1, fa[(kk + 1) & 1]);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) fb[(kk + 1) & 1][j] = make_b(wr[PAR], j, kk + 1, T);
-      } else if constexpr (FMT == QW_FMT_2BIT_G32) {  // the next step's (W of tile kt+1)
+      } else if constexpr (!kTab) {  // the next step's (W of tile kt+1)
         make_tables(wr[PAR ^ 1], T);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) fb0[j] = make_b(wr[PAR ^ 1], j, 0, T);
@@ -609,7 +626,7 @@ __global__ __launch_bounds__(256 * WM) void prefill_w_kernel(PrefillArgs a) {
       // at the next step's start does not wait for X), and X is stored and
       // refilled one slice later (its wait overlaps a slice of products);
       // measured 2% faster for 2-bit, not for the 4-bit formats
-      if constexpr (FMT == QW_FMT_2BIT_G32) {
+      if constexpr (!kTab) {
         if (kk == 0) load_w(kn1, wr[PAR ^ 1]);
         if (kk == 1) {
           store_x(buf ^ 1);
@@ -645,7 +662,7 @@ __global__ __launch_bounds__(256 * WM) void prefill_w_kernel(PrefillArgs a) {
   __syncthreads();  // the NF4 table too
   store_x(0);
   load_x(1);
-  if constexpr (FMT == QW_FMT_2BIT_G32) {
+  if constexpr (!kTab) {
     make_tables(wr[0], T);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) fb0[j] = make_b(wr[0], j, 0, T);
