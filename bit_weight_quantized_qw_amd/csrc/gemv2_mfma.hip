@@ -1159,12 +1159,18 @@ int unsplit_slices(const Args &a, int B, int *xraw, int *bmax_out) {
 }
 
 // Part p of ks: the weight view with its channels and its run of anchor
-// chunks, planned alone; its Mat is a.m[0].
+// chunks, planned alone; its Mat is a.m[0]. The parts of one launch share
+// the CUs (each gets cus / parts-in-its-launch workgroups with
+// proportionally more tiles), so every workgroup prepares x for its own part
+// only; measured on MI355X, giving each part all the CUs instead (one
+// workgroup per CU per part) made every launch prepare x parts times over:
+// 5120x27648 at batches 2 / 4 / 8 ran 40 / 63 / 128 us against 22 / 30 / 62.
 qw_status plan_part(const qw_weight &w, int ks, int p, const uint16_t *x, int cus, Args &a, int &grid) {
   qw_weight pw = w;
   pw.K = w.K / ks;
   void *dummy = nullptr;
-  QW_TRY(plan(&pw, 1, x, &dummy, true, cus, a, grid));
+  const int share = min(kMats, ks - (p / kMats) * kMats);  // parts in p's launch
+  QW_TRY(plan(&pw, 1, x, &dummy, true, max(1, cus / share), a, grid));
   Mat &m = a.m[0];
   const int kp = pw.K;
   m.kbase = p * kp;
@@ -1187,11 +1193,15 @@ qw_status plan_part(const qw_weight &w, int ks, int p, const uint16_t *x, int cu
 }
 
 // K parts for one matrix at batch B: 1 = unsplit, 0 = this kernel does not
-// take the shape. Measured on MI355X, a split pays only where no unsplit
-// pass of two or more batch rows fits (the split's extra workgroups each
-// prepare their share of x for the whole batch, and the parts cost one more
-// launch), and there the fewest parts that fit are fastest. The test hook
-// QW_TUNE_GEMV2_SPLIT = n forces n parts where n is valid.
+// take the shape. Measured on MI355X:
+//  * the split pays where no unsplit pass of two or more batch rows fits;
+//    shapes that fit whole ran as fast or faster whole at batches 2-4 (the
+//    parts add a launch and a reduction), and at batch 1 the parts were no
+//    faster than the vector-ALU kernel on 5120x27648 (19.2 us in 3 parts);
+//  * among the part counts that fit: the fewest launches (kMats parts per
+//    launch), then the most parts (5120x27648 batch 2: 21.7 us in 3 parts,
+//    26.6 in 2, 30.6 in 6; 8192x28672 batch 8: 71.9 us in 8, 82.2 in 7).
+// The test hook QW_TUNE_GEMV2_SPLIT = n forces n parts where n is valid.
 int choose_split_uncached(const qw_weight &w, int B, int cus, int forced) {
   const int K = w.K;
   if (K % 512 != 0) return 0;
@@ -1203,7 +1213,7 @@ int choose_split_uncached(const qw_weight &w, int B, int cus, int forced) {
   const int ns = unsplit_slices(a, B, &xr, &bmax);
   if (ns > 0 && forced <= 1) return 1;
   const int SC = K / 512;
-  int first = 0;
+  int best = 0;
   for (int ks = 2; ks <= kMaxSplit; ++ks) {
     if (SC % ks != 0) continue;
     // every part must fit (their anchor runs differ by up to one chunk)
@@ -1216,10 +1226,11 @@ int choose_split_uncached(const qw_weight &w, int B, int cus, int forced) {
     }
     if (!fit) continue;
     if (forced == ks) return ks;
-    if (first == 0) first = ks;
+    // ks grows: it replaces best unless it needs more launches
+    if (best == 0 || (ks + kMats - 1) / kMats == (best + kMats - 1) / kMats) best = ks;
   }
-  if (ns > 0) return 1;
-  return first;
+  if (ns > 0) return 1;  // a forced count that does not apply
+  return best;
 }
 
 // The choice depends on the shape only, so it is planned once per shape
@@ -1274,8 +1285,8 @@ qw_status launch_split(const qw_weight &w, int ks, const uint16_t *x, int B, voi
   const size_t plane = (size_t)B * w.N;
   if (plane > (size_t)INT32_MAX) return QW_ERR_UNSUPPORTED;  // int indices in the reduction
   Args parts_a[kMaxSplit];
-  int grid_p = 0;
-  for (int p = 0; p < ks; ++p) QW_TRY(plan_part(w, ks, p, x, cus, parts_a[p], grid_p));
+  int grid_p[kMaxSplit];
+  for (int p = 0; p < ks; ++p) QW_TRY(plan_part(w, ks, p, x, cus, parts_a[p], grid_p[p]));
   const bool deep = deep_ring();
   qw_status st = QW_OK;
   for (int p0 = 0; p0 < ks && st == QW_OK; p0 += kMats) {
@@ -1285,12 +1296,12 @@ qw_status launch_split(const qw_weight &w, int ks, const uint16_t *x, int B, voi
     for (int i = 0; i < a.count; ++i) {
       a.m[i] = parts_a[p0 + i].m[0];
       a.m[i].y = parts + (size_t)(p0 + i) * plane;
-      a.m[i].wg_begin = i * grid_p;
+      a.m[i].wg_begin = i * grid_p[p0];
       xo_len = max(xo_len, parts_a[p0 + i].xo_len);
     }
     a.xo_len = xo_len;
     const size_t lds = lds_layout(B, a.K, a.xo_len, a.units_max, 0).total;
-    st = launch_b(a, B, deep, grid_p * a.count, lds, s);
+    st = launch_b(a, B, deep, grid_p[p0] * a.count, lds, s);
   }
   if (st == QW_OK &&
       launch(split_reduce_kernel, (unsigned)((plane + 255) / 256), 256, 0, s, (const float *)parts, ks,
