@@ -1014,13 +1014,15 @@ qw_status launch_b(const Args &a, int B, bool deep, int grid, size_t lds, hipStr
 }
 
 // Waves per tile: a divisor of the super-chunk count minimising the time of
-// the busiest wave of a workgroup of nw waves holding `tw` tiles.
-int pick_splits(int tw, int sc, int nw) {
+// the busiest wave of a workgroup of nw waves holding `tw` tiles, with at
+// most max_units units (tw * w) per workgroup.
+int pick_splits(int tw, int sc, int nw, long max_units = 1L << 30) {
   int best = 1;
   long best_t = -1;
   for (int w = 1; w <= sc; ++w) {
     if (sc % w) continue;
     const long units = (long)tw * w;
+    if (w > 1 && units > max_units) continue;
     const long t = ((units + nw - 1) / nw) * (sc / w);
     if (best_t < 0 || t < best_t) {
       best_t = t;
@@ -1039,9 +1041,21 @@ int pick_splits(int tw, int sc, int nw) {
 // swiglu: ws[0] alone is a merged gate/up matrix (N = 2I, I % 16 == 0); its
 // I / 16 tile pairs are dealt to up to 2 workgroups per CU (as many as the
 // two matrices would take as a grouped launch), within ``budget``.
+// batch > 0: a matrix whose whole batch would miss one pass only through
+// the LDS buffer of partial row sums (many tiles per workgroup times many K
+// splits) gets fewer splits so that it fits: the weights then stream once
+// instead of once per batch slice (27648x5120 batch 8: two 4-row passes,
+// 54.6 us, against one pass). Each matrix's splits depend on itself and the
+// batch only, so grouped and separate launches keep giving the same bits.
+static bool fits_whole(int B, int K, int xo_len, long units) {
+  return (long)B * K <= (long)kXItems * kThreads * 8 &&
+         (lds_layout(B, K, xo_len, (int)units, 1).total <= 160 * 1024 ||
+          lds_layout(B, K, xo_len, (int)units, 0).total <= 160 * 1024);
+}
+
 static qw_status plan(const qw_weight *ws, int count, const uint16_t *x, void *const *ys, bool f32,
                       int cus, Args &a, int &grid, int budget = 1 << 30, int nt = kThreads,
-                      bool swiglu = false) {
+                      bool swiglu = false, int batch = 0) {
   const int K = ws[0].K;
   if (K % 512 != 0 || count > kMats) return QW_ERR_UNSUPPORTED;
   if (swiglu && (count != 1 || ws[0].N % 32 != 0)) return QW_ERR_INVALID_ARG;
@@ -1101,6 +1115,15 @@ static qw_status plan(const qw_weight *ws, int count, const uint16_t *x, void *c
     const int tw = swiglu ? 2 * ((m.tiles / 2 + m.wg_count - 1) / m.wg_count)
                           : (m.tiles + m.wg_count - 1) / m.wg_count;
     m.W = pick_splits(tw, SC, nt / 64);
+    if (batch > 0) {
+      const int npad = m.n_out_pad;
+      const int xo_i = (npad + kAnchorChunk - 1) / kAnchorChunk * kAnchorChunk;
+      long cap = (long)tw * m.W;
+      if (!fits_whole(batch, K, xo_i, cap)) {
+        while (cap > tw && !fits_whole(batch, K, xo_i, cap)) --cap;
+        if (fits_whole(batch, K, xo_i, cap)) m.W = pick_splits(tw, SC, nt / 64, cap);
+      }
+    }
     units_max = max(units_max, tw * m.W);
   }
   a.units_max = units_max;
@@ -1208,7 +1231,7 @@ int choose_split_uncached(const qw_weight &w, int B, int cus, int forced) {
   Args a;
   int grid = 0;
   void *dummy = nullptr;
-  if (plan(&w, 1, nullptr, &dummy, true, cus, a, grid) != QW_OK) return 0;
+  if (plan(&w, 1, nullptr, &dummy, true, cus, a, grid, 1 << 30, kThreads, false, B) != QW_OK) return 0;
   int xr = 1, bmax = 0;
   const int ns = unsplit_slices(a, B, &xr, &bmax);
   if (ns > 0 && forced <= 1) return 1;
@@ -1340,7 +1363,7 @@ qw_status launch(const qw_weight *ws, int count, const uint16_t *x, int B, void 
   const int K = ws[0].K;
   Args a;
   int grid = 0;
-  QW_TRY(plan(ws, count, x, ys, f32, cus, a, grid));
+  QW_TRY(plan(ws, count, x, ys, f32, cus, a, grid, 1 << 30, kThreads, false, B));
   // Widest batch slice whose x (limbs in LDS, raw x in the prologue
   // registers) fits. Batch rows are independent (each is its own row of the
   // product's A operand), so slicing changes no bits.
@@ -1374,7 +1397,7 @@ qw_status launch_swiglu(const qw_weight &w, const uint16_t *x, int B, void *y, b
   Args a;
   int grid = 0;
   void *ys[1] = {y};
-  QW_TRY(plan(&w, 1, x, ys, f32, cus, a, grid, 1 << 30, kThreads, true));
+  QW_TRY(plan(&w, 1, x, ys, f32, cus, a, grid, 1 << 30, kThreads, true, B));
   int xr = 1, bmax = 0;
   int n_slices = unsplit_slices(a, B, &xr, &bmax);
   if (n_slices == 0 && bmax == 1) n_slices = B;  // one row at a time
@@ -1407,7 +1430,7 @@ qw_status launch_int4(const qw_weight &w, const uint16_t *x, int B, void *y, boo
   Args a;
   int grid = 0;
   void *ys[1] = {y};
-  QW_TRY(plan(&w, 1, x, ys, f32, cus, a, grid));
+  QW_TRY(plan(&w, 1, x, ys, f32, cus, a, grid, 1 << 30, kThreads, false, B));
   a.m[0].mask = nullptr;  // anchors: the first n_out positions
   a.m[0].idx = nullptr;
   int xr = 1, bmax = 0;
