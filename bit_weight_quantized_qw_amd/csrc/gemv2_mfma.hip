@@ -41,7 +41,8 @@
 // and are added in a fixed order.
 // The same body serves the merged gate/up product (pairs of gate and up tiles
 // per workgroup, silu(gate) * up in the epilogue), the K parts of wide
-// batches, and the persistent decode stack at the end of this file.
+// batches, the v3.2 INT4 format (kernel_int4), and the persistent decode
+// stack at the end of this file.
 #include <stdlib.h>
 
 #include <mutex>
@@ -648,7 +649,7 @@ __device__ __forceinline__ void body(const Args &a, const int bid, uint8_t *lds)
       if (c.step < L) {
         const int sc = split * L + c.step;
         // chunk ch: this lane's group 16 sc + 4g + ch (code words c_ch), its
-        // nibbles split into the three e2m1 operands; chunks outermost, so
+        // nibbles split into the two e2m1 operands; chunks outermost, so
         // only one chunk's operands are live
         const uint8_t *p_lo = a_ok && !a_hi ? limbs + (size_t)(16 * sc) * 96 + a_lane : zero;
         const uint8_t *p_hi = a_ok && a_hi ? limbs + (size_t)(16 * sc) * 96 + a_lane : zero;

@@ -10,6 +10,10 @@
 // with x_p the activations in permuted channel order (the anchor positions
 // hold u = 8, the zero level, so they add nothing to the first sum).
 //
+// qgemv_int4 runs the matrix-core GEMV's INT4 branch (kernel_int4) wherever
+// K is a multiple of 512 and a batch slice fits it; the vector-ALU kernel of
+// this file takes the other shapes (and the test hook QW_TUNE_INT4_PATH = 1).
+//
 // Work split (as the NF4 GEMV): a workgroup owns a block of rows; workers of
 // W waves walk sub-ranges of them and split K. Lane l of wave w owns the
 // groups h = (j*W + w)*64 + l (32 codes = 16 bytes, so every code load of a
