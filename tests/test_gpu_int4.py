@@ -84,8 +84,12 @@ def _gemv(pw, x_p16, f32=True):
     return y.float().cpu().numpy()
 
 
+# K a multiple of 512 runs on the matrix cores (one super-chunk, one row,
+# a ragged tile, anchors ending inside and at the edge of a group), the
+# others on the vector ALUs
 @pytest.mark.parametrize("N,K,n_out", [(200, 3072, 30), (77, 1024, 0), (1, 32, 0), (33, 160, 1),
-                                       (300, 8192, 81), (50, 16384, 163)])
+                                       (300, 8192, 81), (50, 16384, 163), (1, 512, 0), (17, 512, 5),
+                                       (16, 1536, 32)])
 @pytest.mark.parametrize("B", [1, 2, 3, 5, 8])
 def test_gemv_small(N, K, n_out, B):
     W = inputs.weight(N, K, workload=114)
